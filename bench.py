@@ -1,0 +1,258 @@
+#!/usr/bin/env python3
+"""Throughput of one AuraFlow transformer forward on one MI355X.
+
+Default workload: 1024 x 1024 image (latent 4 x 128 x 128 -> 4096 image tokens,
+8 register + 256 text tokens, sequence 4360), CFG batch 2 ([uncond; cond] sharing
+one latent and timestep), 4 joint + 32 single blocks, d = 3072, bf16 weights
+drawn from the seeded synthetic recipe. One step = one full forward through the
+C-ABI (every kernel of the path), inputs already resident in HBM.
+
+Prints one JSON line. The timed region is bracketed by synchronisation and
+measured with HIP events on the stream the kernels run on.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+
+def _cpu_threads():
+    try:
+        n = len(os.sched_getaffinity(0))
+    except Exception:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+# BLAS threads for the CPU-baseline leg (must be set before numpy loads).
+os.environ.setdefault("OPENBLAS_NUM_THREADS", str(_cpu_threads()))
+os.environ.setdefault("OMP_NUM_THREADS", str(_cpu_threads()))
+
+import numpy as np  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+
+WORKLOADS = {
+    # name: (B, latent H, latent W, text T)
+    "1024": (2, 128, 128, 256),
+    "1536": (2, 192, 192, 256),
+}
+
+
+def forward_flops(d, F, L, B, S, T, Dtxt, Nimg, patch_dim):
+    """Algorithmic FLOPs of one forward: QKV, attention (QK^T and PV), out-proj and
+    FFN per block, plus caption projection, patch embed and output projection."""
+    per_block = 2 * S * d * 3 * d + 4 * S * S * d + 2 * S * d * d + 6 * S * d * F
+    return B * L * per_block + B * (2 * T * Dtxt * d + 4 * Nimg * patch_dim * d)
+
+
+def class_work(name, d, F, B, S):
+    """(algorithmic FLOPs or bytes per launch, unit kind) for a kernel class."""
+    M = B * S
+    if name == "gemm_qkv":
+        return 2.0 * M * d * 3 * d, "mfma"
+    if name == "gemm_out":
+        return 2.0 * M * d * d, "mfma"
+    if name == "gemm_ffn_up":
+        return 2.0 * M * d * 2 * F, "mfma"
+    if name == "gemm_ffn_down":
+        return 2.0 * M * F * d, "mfma"
+    if name == "attention":
+        return 4.0 * B * S * S * d, "mfma"
+    if name == "ln_modulate":
+        return float(M * d * 4 + M * d * 2), "hbm"   # fp32 residual in, bf16 out
+    return None, None
+
+
+def cpu_baseline(workload, threads):
+    """The oracle (fp32 numpy) on a bounded sample: embedding + one joint block +
+    one single block at the full workload shape; forward time extrapolated as
+    embed + 4 joint + 32 single."""
+    import oracle
+    import seeded_inputs
+    from oracle import transformer as T_
+
+    B, H, W, T = WORKLOADS[workload]
+    cfg = oracle.FULL
+    lat = np.concatenate([seeded_inputs.latents(1, 4, H, W)] * B)
+    tau = np.full(B, 0.5, np.float32)
+    text = oracle.round_bf16(seeded_inputs.text_embeddings(B, T, cfg.joint_attention_dim))
+    mask = seeded_inputs.length_mask(seeded_inputs.valid_lengths(B, 16, T), T)
+    names = ["t_w1", "t_b1", "t_w2", "t_b2", "pe_w", "pe_b", "pos_embed", "ctx_w", "registers"]
+    blk_names = [n for n, _, _ in oracle.weight_specs(cfg) if n.startswith(("joint0.", "single0."))]
+    Wseed = oracle.Weights.seeded(cfg, seed=0, bf16=True)
+    t0 = time.time()
+    cache = {n: Wseed[n] for n in names + blk_names}
+    gen_s = time.time() - t0
+    W = oracle.Weights.from_dict(cfg, cache)
+    f32 = np.float32
+    t0 = time.time()
+    temb, xt, xi, kv = oracle.embed(cfg, W, lat, tau, text, mask, f32)
+    t_embed = time.time() - t0
+    blk = lambda p: {k: W[p + k] for k in ("ada", "wq", "wk", "wv", "wo", "ff1", "ff2", "ff3")}
+    t0 = time.time()
+    xt2, xi2 = oracle.joint_block(cfg, blk("joint0.img."), blk("joint0.txt."), temb, xt, xi, kv, f32)
+    t_joint = time.time() - t0
+    x = np.concatenate([xt2, xi2], axis=1)
+    t0 = time.time()
+    oracle.single_block(cfg, blk("single0."), temb, x, kv, f32)
+    t_single = time.time() - t0
+    t_fwd = t_embed + cfg.num_mmdit_layers * t_joint + cfg.num_single_dit_layers * t_single
+    return {
+        "value": 1.0 / t_fwd, "unit": "forwards/s", "cores": threads, "kind": "oracle",
+        "sample": (f"numpy fp32 oracle, BLAS threads={threads}: embedding ({t_embed:.2f} s) + 1 joint block "
+                   f"({t_joint:.2f} s) + 1 single block ({t_single:.2f} s) at the full {workload}^2 CFG-batch-2 "
+                   f"shape; forward extrapolated as embed + 4 joint + 32 single = {t_fwd:.1f} s; weight "
+                   f"generation ({gen_s:.1f} s) excluded"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="1024")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-profile", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: the forward runs on a single MI355X and this build has no "
+              f"multi-GPU path (--gpus {args.gpus} requested).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import flow_matching_mmdit_amd as pkg
+    if not os.path.exists(pkg.LIB_PATH):
+        from flow_matching_mmdit_amd import build as _b
+        _b.build()
+    from flow_matching_mmdit_amd import binding as af
+    import seeded_inputs
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    B, H, W, T = WORKLOADS[args.workload]
+    cfg = af.make_config(max_batch=B, max_latent_h=H, max_latent_w=W, max_text_len=T)
+    d = cfg.num_attention_heads * cfg.attention_head_dim
+    F = ((8 * d) // 3 + 255) // 256 * 256
+    L = cfg.num_mmdit_layers + cfg.num_single_dit_layers
+    Nimg = (H // 2) * (W // 2)
+    S = cfg.num_register_tokens + T + Nimg
+
+    t0 = time.time()
+    model = af.AuraFlowModel(cfg, 0)
+    model.load_seeded_weights(seed=0, threads=_cpu_threads())
+    torch.cuda.synchronize()
+    setup_s = time.time() - t0
+    print(f"[bench] weights ready in {setup_s:.1f} s", file=sys.stderr, flush=True)
+
+    # Workload inputs: CFG pair sharing one latent and timestep, independent text, padded text masked.
+    lat1 = seeded_inputs.latents(B // 2, 4, H, W)
+    lat = torch.from_numpy(np.concatenate([lat1, lat1])).cuda()
+    t = seeded_inputs.timesteps_uniform(B // 2) / 1000.0
+    tau = torch.from_numpy(np.concatenate([t, t]).astype(np.float32)).cuda()
+    text = torch.from_numpy(seeded_inputs.text_embeddings(B, T, cfg.joint_attention_dim)).cuda()
+    mask = torch.from_numpy(seeded_inputs.length_mask(seeded_inputs.valid_lengths(B, 16, T), T)).cuda()
+    out = torch.empty((B, 4, H, W), dtype=torch.float32, device="cuda")
+
+    for _ in range(args.warmup):
+        model.forward(lat, tau, text, mask, out=out)
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done", file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        model.forward(lat, tau, text, mask, out=out)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    ms_per_step = ms / args.steps
+    value = 1000.0 / ms_per_step
+    flops = forward_flops(d, F, L, B, S, T, cfg.joint_attention_dim, Nimg, 16)
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+    assert torch.isfinite(out).all().item(), "non-finite output"
+    print(f"[bench] {ms_per_step:.2f} ms/forward, {tflops:.1f} TFLOP/s", file=sys.stderr, flush=True)
+
+    kernels, roofline = {}, None
+    if not args.no_profile:
+        af.af_profile(model, True)
+        for _ in range(args.steps):
+            model.forward(lat, tau, text, mask, out=out)
+        torch.cuda.synchronize()
+        prof = af.af_profile_read(model)
+        af.af_profile(model, False)
+        best = None
+        for name, (kms, n) in prof.items():
+            if n == 0:
+                continue
+            work, kind = class_work(name, d, F, B, S)
+            entry = {"ms_per_forward": kms / args.steps, "launches_per_forward": n / args.steps,
+                     "avg_launch_ms": kms / n}
+            if work is not None:
+                rate = work / (kms / n * 1e-3)
+                if kind == "mfma":
+                    entry["tflops"] = rate / 1e12
+                    entry["frac_peak"] = rate / 1e12 / PEAK_BF16_TFLOPS
+                else:
+                    entry["gbs"] = rate / 1e9
+                    entry["frac_peak"] = rate / 1e9 / PEAK_HBM_GBS
+                if best is None or kms > best[1]:
+                    best = (name, kms, n, work, kind)
+            kernels[name] = entry
+        if best is not None:
+            name, kms, n, work, kind = best
+            avg = kms / n * 1e-3
+            if kind == "mfma":
+                roofline = {"bound": "mfma", "kernel": name, "achieved": work / avg / 1e12,
+                            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                            "frac": work / avg / 1e12 / PEAK_BF16_TFLOPS, "traffic": None,
+                            "avg_launch_ms": avg * 1e3, "work_per_launch": work}
+            else:
+                roofline = {"bound": "hbm", "kernel": name, "achieved": work / avg / 1e9, "peak": PEAK_HBM_GBS,
+                            "unit": "GB/s", "frac": work / avg / 1e9 / PEAK_HBM_GBS, "traffic": None,
+                            "avg_launch_ms": avg * 1e3, "work_per_launch": work}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print(f"[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(args.workload, _cpu_threads())
+
+    res = {
+        "metric": "AuraFlow transformer forwards/s at 1024² CFG batch 2; TFLOP/s as % of bf16 peak",
+        "value": value,
+        "unit": "forwards/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"AuraFlow transformer forward at {args.workload}x{args.workload} "
+                               f"(latent 4x{H}x{W}: {Nimg} image + 8 register + {T} text tokens), CFG batch {B}, "
+                               f"4 joint + 32 single blocks, d=3072, 12x256 heads, FFN 8192, seeded random "
+                               f"bf16 weights (6.86B params), padded text masked",
+                   "global_batch": B, "seq_len": S, "parallelism": "single GPU"},
+        "tflops": tflops,
+        "pct_peak_bf16": 100.0 * tflops / PEAK_BF16_TFLOPS,
+        "flops_per_forward": flops,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+        "setup_s": setup_s,
+    }
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,85 @@
+// Host-side launch interface between the executor (af_model.hip) and the kernel
+// translation units. Every launcher validates nothing: the executor has already
+// checked shapes on the host. Each returns the launch's hipError_t.
+#pragma once
+#include <hip/hip_runtime.h>
+#include "af_device.h"
+#include "../../include/auraflow.h"
+
+namespace af {
+
+// ------------------------------------------------------------------ GEMM (C = A B^T)
+enum GemmEpi {
+    EPI_STORE = 0,          // C[m, n] = acc (dtype of the path)
+    EPI_STORE_MAPPED = 1,   // resid[map(m), n] = acc (fp32), map = (m/seg_len)*seg_stride + seg_off + m%seg_len
+    EPI_GATED_RESID = 2,    // resid[row0 + m, n] += gate[batch(row0 + m), n] * acc
+    EPI_QKV = 3,            // bf16 only: per-head LayerNorm of q, k; q, k -> [B,H,S_pad,hd]; v -> v^T [B,H,hd,S_pad]
+    EPI_SWIGLU = 4          // bf16 only: h[m, f] = silu(acc[gate col]) * acc[up col], 32-column interleave
+};
+
+struct GemmGroup {
+    const void* A; long lda;   // [M, K] row-major
+    const void* W; long ldw;   // [N, K] row-major (weights, y = x W^T)
+    int M;
+    int row0;                  // residual row of GEMM row 0 (GATED_RESID, QKV)
+    int gate_off;              // column of gate vector inside a mod row (GATED_RESID)
+};
+
+struct GemmLaunch {
+    GemmGroup g[2];
+    int ngroups;
+    int N, K;
+    int epi;
+    void* C; long ldc;                 // STORE / SWIGLU output
+    float* resid;                      // MAPPED / GATED_RESID output, leading dim N
+    const float* mod; long mod_stride; // gate vectors: mod[b * mod_stride + gate_off + n]
+    RowGeom geom;
+    int seg_len, seg_stride, seg_off;  // STORE_MAPPED row map
+    void* q; void* k; void* vt;        // QKV outputs
+    int H, hd, S_pad;
+    float eps;
+};
+
+hipError_t gemm_bf16(const GemmLaunch& L, hipStream_t s);
+hipError_t gemm_f32(const GemmLaunch& L, hipStream_t s);
+
+// ------------------------------------------------------------------ attention
+// q, k: [B, H, S_pad, hd]; v^T: [B, H, hd, S_pad] (bf16 path) or v: [B, H, S_pad, hd] (fp32 path);
+// bias: [B, S_pad] additive key bias (0 or -inf); o: [M, d] in residual row order.
+hipError_t attention_bf16(const bf16_t* q, const bf16_t* k, const bf16_t* vt, const float* bias,
+                          RowGeom g, int H, int S_pad, bf16_t* o, int d, hipStream_t s);
+hipError_t attention_f32(const float* q, const float* k, const float* v, const float* bias,
+                         RowGeom g, int H, int hd, int S_pad, float* o, int d, hipStream_t s);
+
+// ------------------------------------------------------------------ small kernels
+hipError_t timestep_features(const float* tau, int B, int half, float tscale, float* e, hipStream_t s);
+// y[b, n] = sum_k W[n, k] * act(x[b, k]) + bias[n]   (act = silu when silu_in)
+hipError_t gemv(const float* x, int B, int K, const void* W, af_dtype wdt, int N,
+                const void* bias, int silu_in, float* y, hipStream_t s);
+hipError_t patch_embed(const float* lat, int C, int H, int W, int p, const void* pe_w,
+                       const void* pe_b, af_dtype wdt, const float* pos, int G, float* resid,
+                       RowGeom g, int d, hipStream_t s);
+hipError_t copy_registers(const void* reg, af_dtype wdt, int R, float* resid, RowGeom g, int d,
+                          hipStream_t s);
+hipError_t f32_to_bf16(const float* src, bf16_t* dst, long n, hipStream_t s);
+hipError_t key_bias(const uint8_t* mask, int T, int R, RowGeom g, int S_pad, float* bias,
+                    hipStream_t s);
+// out[r] = LN(x[r]) * (1 + scale) + shift; rows r < split use offsets (sh_a, sc_a), others (sh_b, sc_b)
+hipError_t ln_modulate(const float* x, int M, int d, RowGeom g, int split, const float* mod,
+                       long mod_stride, int sh_a, int sc_a, int sh_b, int sc_b, void* out,
+                       af_dtype odt, float eps, hipStream_t s);
+hipError_t prefinal_project(const float* resid, RowGeom g, int d, const float* mod, long mod_stride,
+                            int sc_off, int sh_off, const void* Wout, af_dtype wdt, int Cout, int p,
+                            int h, int w, float* out, hipStream_t s);
+hipError_t euler_cfg(float* x, const float* v, long n, float dt, float guidance, int cfg_on,
+                     hipStream_t s);
+enum PackLayout { PACK_PLAIN = 0, PACK_FFN_GATE = 1, PACK_FFN_UP = 2 };
+// Converts src[0, n) (a slice of one canonical tensor starting at element `first`) into dst.
+hipError_t pack_weights(const float* src, long n, long first, void* dst, af_dtype ddt, int layout,
+                        int cols, hipStream_t s);
+hipError_t taps_permute(const float* resid, RowGeom g, int d, float* out, hipStream_t s);
+hipError_t qknorm_scatter_f32(const float* raw, int M, RowGeom g, int H, int hd, int S_pad,
+                              float eps, float* q, float* k, float* v, int row0, hipStream_t s);
+hipError_t swiglu_f32(const float* raw, int M, int F, float* h, hipStream_t s);
+
+}  // namespace af

@@ -1,0 +1,557 @@
+// Bandwidth- and latency-bound kernels of the AuraFlow forward on gfx950:
+// timestep features, GEMV (timestep MLP and every block's adaLN modulation at
+// once), patch embedding with the centre-cropped position table, register
+// tokens, key-padding bias, fused fp32 LayerNorm + shift/scale modulation,
+// pre-final modulation fused with the output projection and unpatchify, the
+// Euler + CFG update, weight packing and fp32-path helpers.
+//
+// Page tags: [PIPE], [TRANS], [DEEP] as listed in include/auraflow.h.
+#include "af_internal.h"
+
+namespace af {
+
+// ============================================================================ timestep features
+// [TRANS] 前向传播流程 (Timesteps, 256 channels): u = timestep_scale * tau;
+// e = [cos(u f_k) (k < half), sin(u f_k)], f_k = 10000^(-k/half). Computed in
+// double so the features carry no fp32 argument-rounding error (u reaches 1000 rad).
+__global__ void k_timestep_features(const float* __restrict__ tau, int B, int half, double tscale,
+                                    float* __restrict__ e) {
+    int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= B * half) return;
+    int b = i / half, k = i % half;
+    double u = tscale * (double)tau[b];
+    double f = exp(-log(10000.0) * (double)k / (double)half);
+    double a = u * f;
+    e[b * 2 * half + k] = (float)cos(a);
+    e[b * 2 * half + half + k] = (float)sin(a);
+}
+
+hipError_t timestep_features(const float* tau, int B, int half, float tscale, float* e, hipStream_t s) {
+    int n = B * half;
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_timestep_features, dim3((n + 255) / 256), dim3(256), 0, s, tau, B, half,
+                       (double)tscale, e);
+    return hipGetLastError();
+}
+
+// ============================================================================ GEMV
+// y[b, n] = sum_k W[n, k] act(x[b, k]) + bias[n]. One wave per output row
+// (grid-stride), each lane owning fixed 16-byte chunks of k so the activation
+// values stay in registers across rows. Batches go in passes of BC.
+template <typename WT> struct WChunk;
+template <> struct WChunk<bf16_t> {
+    static constexpr int E = 8;
+    __device__ static void load(const bf16_t* p, float* o) {
+        uint4 v = *reinterpret_cast<const uint4*>(p);
+        uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            o[2 * i] = __uint_as_float(w[i] << 16);
+            o[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+        }
+    }
+    __device__ static float one(const bf16_t* p) { return bf2f(*p); }
+};
+template <> struct WChunk<float> {
+    static constexpr int E = 4;
+    __device__ static void load(const float* p, float* o) {
+        float4 v = *reinterpret_cast<const float4*>(p);
+        o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+    }
+    __device__ static float one(const float* p) { return *p; }
+};
+
+template <typename WT, int BC, int MAXI>
+__global__ __launch_bounds__(256) void k_gemv(const float* __restrict__ x, int B, int K,
+                                              const WT* __restrict__ W, int N,
+                                              const WT* __restrict__ bias, int silu_in,
+                                              float* __restrict__ y, int b0) {
+    constexpr int E = WChunk<WT>::E;
+    const int lane = threadIdx.x & 63;
+    const int nb = min(BC, B - b0);
+    float xr[MAXI][BC][E];
+#pragma unroll
+    for (int i = 0; i < MAXI; ++i) {
+        int k0 = (lane + 64 * i) * E;
+#pragma unroll
+        for (int b = 0; b < BC; ++b)
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                float v = 0.f;
+                if (b < nb && k0 + e < K) {
+                    v = x[(long)(b0 + b) * K + k0 + e];
+                    if (silu_in) v = silu_f(v);
+                }
+                xr[i][b][e] = v;
+            }
+    }
+    const int wave = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+    const int nwaves = (gridDim.x * blockDim.x) >> 6;
+    for (int n = wave; n < N; n += nwaves) {
+        const WT* row = W + (long)n * K;
+        float acc[BC];
+#pragma unroll
+        for (int b = 0; b < BC; ++b) acc[b] = 0.f;
+#pragma unroll
+        for (int i = 0; i < MAXI; ++i) {
+            int k0 = (lane + 64 * i) * E;
+            if (k0 < K) {
+                float w[E];
+                WChunk<WT>::load(row + k0, w);
+#pragma unroll
+                for (int b = 0; b < BC; ++b)
+#pragma unroll
+                    for (int e = 0; e < E; ++e) acc[b] += w[e] * xr[i][b][e];
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < BC; ++b) acc[b] = wave_sum(acc[b]);
+        if (lane == 0) {
+            float bb = bias ? WChunk<WT>::one(bias + n) : 0.f;
+            for (int b = 0; b < nb; ++b) y[(long)(b0 + b) * N + n] = acc[b] + bb;
+        }
+    }
+}
+
+hipError_t gemv(const float* x, int B, int K, const void* W, af_dtype wdt, int N, const void* bias,
+                int silu_in, float* y, hipStream_t s) {
+    if (B == 0 || N == 0) return hipSuccess;
+    constexpr int BC = 2;
+    int blocks = (N + 3) / 4;
+    if (blocks > 4096) blocks = 4096;
+    for (int b0 = 0; b0 < B; b0 += BC) {
+        if (wdt == AF_BF16)
+            hipLaunchKernelGGL((k_gemv<bf16_t, BC, 8>), dim3(blocks), dim3(256), 0, s, x, B, K,
+                               (const bf16_t*)W, N, (const bf16_t*)bias, silu_in, y, b0);
+        else
+            hipLaunchKernelGGL((k_gemv<float, BC, 16>), dim3(blocks), dim3(256), 0, s, x, B, K,
+                               (const float*)W, N, (const float*)bias, silu_in, y, b0);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+// ============================================================================ patch embed
+// [PIPE] 深入源码 (Patch Embed) / [TRANS] 核心子模块架构 (Patch Embedding): the
+// latent is cut into p x p patches (feature order channel, row-in-patch,
+// column-in-patch), projected by a Linear with bias, and the learned position
+// row of the centre crop of the G x G table is added. Token t = i*w + j lands in
+// residual row (b, Nt + t). One thread per output column; the patch vectors
+// of a run of tokens are staged in LDS.
+constexpr int PE_ROWS = 64;
+constexpr int PE_MAXF = 64;
+
+template <typename WT>
+__global__ __launch_bounds__(256) void k_patch_embed(const float* __restrict__ lat, int C, int H, int W,
+                                                     int p, const WT* __restrict__ pe_w,
+                                                     const WT* __restrict__ pe_b,
+                                                     const float* __restrict__ pos, int G,
+                                                     float* __restrict__ resid, RowGeom g, int d) {
+    __shared__ float sp[PE_ROWS][PE_MAXF];
+    const int Pd = C * p * p;
+    const int h = H / p, w = W / p;
+    const int ntok = h * w;
+    const int b = blockIdx.z;
+    const int t0 = blockIdx.y * PE_ROWS;
+    const int c = blockIdx.x * blockDim.x + threadIdx.x;
+    for (int i = threadIdx.x; i < PE_ROWS * Pd; i += blockDim.x) {
+        int r = i / Pd, f = i % Pd;
+        int t = t0 + r;
+        float v = 0.f;
+        if (t < ntok) {
+            int ti = t / w, tj = t % w;
+            int ch = f / (p * p), py = (f / p) % p, px = f % p;
+            v = lat[(((long)b * C + ch) * H + ti * p + py) * W + tj * p + px];
+        }
+        sp[r][f] = v;
+    }
+    __syncthreads();
+    if (c >= d) return;
+    float wr[PE_MAXF];
+#pragma unroll
+    for (int f = 0; f < PE_MAXF; ++f) wr[f] = f < Pd ? WChunk<WT>::one(pe_w + (long)c * Pd + f) : 0.f;
+    const float bc = WChunk<WT>::one(pe_b + c);
+    const int r0 = (G - h) / 2, c0 = (G - w) / 2;
+    for (int r = 0; r < PE_ROWS; ++r) {
+        int t = t0 + r;
+        if (t >= ntok) break;
+        float acc = bc;
+#pragma unroll
+        for (int f = 0; f < PE_MAXF; ++f) acc += wr[f] * sp[r][f];
+        int ti = t / w, tj = t % w;
+        long pidx = (long)(r0 + ti) * G + (c0 + tj);
+        acc += pos[pidx * d + c];
+        resid[(long)g.row_of(b, g.Nt + t) * d + c] = acc;
+    }
+}
+
+hipError_t patch_embed(const float* lat, int C, int H, int W, int p, const void* pe_w, const void* pe_b,
+                       af_dtype wdt, const float* pos, int G, float* resid, RowGeom g, int d,
+                       hipStream_t s) {
+    int ntok = (H / p) * (W / p);
+    if (g.B == 0 || ntok == 0) return hipSuccess;
+    dim3 grid((d + 255) / 256, (ntok + PE_ROWS - 1) / PE_ROWS, g.B);
+    if (wdt == AF_BF16)
+        hipLaunchKernelGGL(k_patch_embed<bf16_t>, grid, dim3(256), 0, s, lat, C, H, W, p,
+                           (const bf16_t*)pe_w, (const bf16_t*)pe_b, pos, G, resid, g, d);
+    else
+        hipLaunchKernelGGL(k_patch_embed<float>, grid, dim3(256), 0, s, lat, C, H, W, p,
+                           (const float*)pe_w, (const float*)pe_b, pos, G, resid, g, d);
+    return hipGetLastError();
+}
+
+// ============================================================================ register tokens
+// [TRANS] 核心子模块架构 (Register Tokens): R learned tokens at the head of the text sequence.
+template <typename WT>
+__global__ void k_registers(const WT* __restrict__ reg, int R, float* __restrict__ resid, RowGeom g, int d) {
+    long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    long n = (long)g.B * R * d;
+    if (i >= n) return;
+    int c = i % d;
+    int r = (i / d) % R;
+    int b = i / ((long)R * d);
+    resid[(long)g.row_of(b, r) * d + c] = WChunk<WT>::one(reg + (long)r * d + c);
+}
+
+hipError_t copy_registers(const void* reg, af_dtype wdt, int R, float* resid, RowGeom g, int d,
+                          hipStream_t s) {
+    long n = (long)g.B * R * d;
+    if (n == 0) return hipSuccess;
+    dim3 grid((unsigned)((n + 255) / 256));
+    if (wdt == AF_BF16)
+        hipLaunchKernelGGL(k_registers<bf16_t>, grid, dim3(256), 0, s, (const bf16_t*)reg, R, resid, g, d);
+    else
+        hipLaunchKernelGGL(k_registers<float>, grid, dim3(256), 0, s, (const float*)reg, R, resid, g, d);
+    return hipGetLastError();
+}
+
+// ============================================================================ fp32 -> bf16 (text)
+__global__ void k_f32_to_bf16(const float* __restrict__ src, bf16_t* __restrict__ dst, long n) {
+    long i = ((long)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+    if (i + 3 < n) {
+        float4 v = *reinterpret_cast<const float4*>(src + i);
+        uint2 o = {pack2bf(v.x, v.y), pack2bf(v.z, v.w)};
+        *reinterpret_cast<uint2*>(dst + i) = o;
+    } else {
+        for (; i < n; ++i) dst[i] = f2bf(src[i]);
+    }
+}
+
+hipError_t f32_to_bf16(const float* src, bf16_t* dst, long n, hipStream_t s) {
+    if (n == 0) return hipSuccess;
+    long threads = (n + 3) / 4;
+    hipLaunchKernelGGL(k_f32_to_bf16, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, src, dst, n);
+    return hipGetLastError();
+}
+
+// ============================================================================ key-padding bias
+// Sequence position s of sample b: registers [0, R) always valid, text [R, Nt)
+// valid where mask[b, s - R] != 0, image [Nt, S) always valid, padding
+// [S, S_pad) never valid. Valid -> 0, excluded -> -inf.
+__global__ void k_key_bias(const uint8_t* __restrict__ mask, int T, int R, RowGeom g, int S_pad,
+                           float* __restrict__ bias) {
+    long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (long)g.B * S_pad) return;
+    int b = i / S_pad, s = i % S_pad;
+    bool valid;
+    if (s >= g.S()) valid = false;
+    else if (s >= R && s < g.Nt) valid = mask == nullptr || mask[(long)b * T + (s - R)] != 0;
+    else valid = true;
+    bias[i] = valid ? 0.f : -INFINITY;
+}
+
+hipError_t key_bias(const uint8_t* mask, int T, int R, RowGeom g, int S_pad, float* bias, hipStream_t s) {
+    long n = (long)g.B * S_pad;
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_key_bias, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, mask, T, R, g,
+                       S_pad, bias);
+    return hipGetLastError();
+}
+
+// ============================================================================ LayerNorm + modulate
+// [TRANS] 核心子模块架构 (调制与归一化): FP32 LayerNorm (no affine, biased
+// variance, eps) followed by x (1 + scale) + shift with the block's adaLN
+// vectors. One wave per row, the row held in registers (d <= 4096), two-pass
+// mean / variance.
+template <typename OT> __device__ __forceinline__ void store4(OT* p, float a, float b, float c, float d);
+template <> __device__ __forceinline__ void store4<bf16_t>(bf16_t* p, float a, float b, float c, float d) {
+    uint2 o = {pack2bf(a, b), pack2bf(c, d)};
+    *reinterpret_cast<uint2*>(p) = o;
+}
+template <> __device__ __forceinline__ void store4<float>(float* p, float a, float b, float c, float d) {
+    *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
+}
+
+template <typename OT>
+__global__ __launch_bounds__(256) void k_ln_modulate(const float* __restrict__ x, int M, int d, RowGeom g,
+                                                     int split, const float* __restrict__ mod,
+                                                     long mod_stride, int sh_a, int sc_a, int sh_b,
+                                                     int sc_b, OT* __restrict__ out, float eps) {
+    constexpr int MAXV = 16;  // float4 per lane -> d <= 4096
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= M) return;
+    const int nv = d / 4;
+    const float* xr = x + (long)row * d;
+    float4 v[MAXV];
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i) {
+        int c4 = lane + 64 * i;
+        if (c4 < nv) {
+            v[i] = reinterpret_cast<const float4*>(xr)[c4];
+            sum += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+        } else {
+            v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    }
+    const float mean = wave_sum(sum) / (float)d;
+    float sq = 0.f;
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i) {
+        int c4 = lane + 64 * i;
+        if (c4 < nv) {
+            float a = v[i].x - mean, b = v[i].y - mean, c = v[i].z - mean, e = v[i].w - mean;
+            sq += (a * a + b * b) + (c * c + e * e);
+        }
+    }
+    const float rstd = rsqrtf(wave_sum(sq) / (float)d + eps);
+    const int bidx = g.batch_of(row);
+    const bool first = row < split;
+    const float* shp = mod + (long)bidx * mod_stride + (first ? sh_a : sh_b);
+    const float* scp = mod + (long)bidx * mod_stride + (first ? sc_a : sc_b);
+    OT* orow = out + (long)row * d;
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i) {
+        int c4 = lane + 64 * i;
+        if (c4 < nv) {
+            float4 sh = reinterpret_cast<const float4*>(shp)[c4];
+            float4 sc = reinterpret_cast<const float4*>(scp)[c4];
+            store4<OT>(orow + 4 * c4, (v[i].x - mean) * rstd * (1.f + sc.x) + sh.x,
+                       (v[i].y - mean) * rstd * (1.f + sc.y) + sh.y,
+                       (v[i].z - mean) * rstd * (1.f + sc.z) + sh.z,
+                       (v[i].w - mean) * rstd * (1.f + sc.w) + sh.w);
+        }
+    }
+}
+
+hipError_t ln_modulate(const float* x, int M, int d, RowGeom g, int split, const float* mod, long mod_stride,
+                       int sh_a, int sc_a, int sh_b, int sc_b, void* out, af_dtype odt, float eps,
+                       hipStream_t s) {
+    if (M == 0) return hipSuccess;
+    dim3 grid((M + 3) / 4);
+    if (odt == AF_BF16)
+        hipLaunchKernelGGL(k_ln_modulate<bf16_t>, grid, dim3(256), 0, s, x, M, d, g, split, mod, mod_stride,
+                           sh_a, sc_a, sh_b, sc_b, (bf16_t*)out, eps);
+    else
+        hipLaunchKernelGGL(k_ln_modulate<float>, grid, dim3(256), 0, s, x, M, d, g, split, mod, mod_stride,
+                           sh_a, sc_a, sh_b, sc_b, (float*)out, eps);
+    return hipGetLastError();
+}
+
+// ============================================================================ pre-final + proj_out + unpatchify
+// [TRANS] 核心子模块架构 (调制与归一化) and 前向传播流程: y = x (1 + scale) + shift
+// on the image rows (modulation only), z = y W_out^T (no bias), and z's
+// features (row-in-patch, column-in-patch, channel) scattered back to
+// [B, C_out, H, W]. One wave per image token; fp32 throughout.
+template <typename WT>
+__global__ __launch_bounds__(256) void k_prefinal_project(const float* __restrict__ resid, RowGeom g, int d,
+                                                          const float* __restrict__ mod, long mod_stride,
+                                                          int sc_off, int sh_off, const WT* __restrict__ Wout,
+                                                          int Cout, int p, int h, int w,
+                                                          float* __restrict__ out) {
+    constexpr int MAXV = 16;
+    constexpr int MAXO = 64;
+    const int lane = threadIdx.x & 63;
+    const int wave = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+    const int nwaves = (gridDim.x * blockDim.x) >> 6;
+    const int ntok = g.B * g.Ni;
+    const int nv = d / 4;
+    const int Pout = p * p * Cout;
+    for (int t = wave; t < ntok; t += nwaves) {
+        const int b = t / g.Ni, tok = t % g.Ni;
+        const float* xr = resid + (long)(g.B * g.Nt + t) * d;
+        const float* sc = mod + (long)b * mod_stride + sc_off;
+        const float* sh = mod + (long)b * mod_stride + sh_off;
+        float4 y[MAXV];
+#pragma unroll
+        for (int i = 0; i < MAXV; ++i) {
+            int c4 = lane + 64 * i;
+            if (c4 < nv) {
+                float4 xv = reinterpret_cast<const float4*>(xr)[c4];
+                float4 s4 = reinterpret_cast<const float4*>(sc)[c4];
+                float4 h4 = reinterpret_cast<const float4*>(sh)[c4];
+                y[i] = make_float4(xv.x * (1.f + s4.x) + h4.x, xv.y * (1.f + s4.y) + h4.y,
+                                   xv.z * (1.f + s4.z) + h4.z, xv.w * (1.f + s4.w) + h4.w);
+            } else {
+                y[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+        }
+        const int ti = tok / w, tj = tok % w;
+        const int H = h * p, W = w * p;
+        for (int o = 0; o < Pout && o < MAXO; ++o) {
+            const WT* wr = Wout + (long)o * d;
+            float acc = 0.f;
+#pragma unroll
+            for (int i = 0; i < MAXV; ++i) {
+                int c4 = lane + 64 * i;
+                if (c4 < nv) {
+                    int c = 4 * c4;
+                    acc += y[i].x * WChunk<WT>::one(wr + c) + y[i].y * WChunk<WT>::one(wr + c + 1) +
+                           y[i].z * WChunk<WT>::one(wr + c + 2) + y[i].w * WChunk<WT>::one(wr + c + 3);
+                }
+            }
+            acc = wave_sum(acc);
+            if (lane == 0) {
+                int py = o / (p * Cout), px = (o / Cout) % p, ch = o % Cout;
+                out[(((long)b * Cout + ch) * H + ti * p + py) * W + tj * p + px] = acc;
+            }
+        }
+    }
+}
+
+hipError_t prefinal_project(const float* resid, RowGeom g, int d, const float* mod, long mod_stride, int sc_off,
+                            int sh_off, const void* Wout, af_dtype wdt, int Cout, int p, int h, int w,
+                            float* out, hipStream_t s) {
+    int ntok = g.B * g.Ni;
+    if (ntok == 0) return hipSuccess;
+    int blocks = (ntok + 3) / 4;
+    if (blocks > 2048) blocks = 2048;
+    if (wdt == AF_BF16)
+        hipLaunchKernelGGL(k_prefinal_project<bf16_t>, dim3(blocks), dim3(256), 0, s, resid, g, d, mod,
+                           mod_stride, sc_off, sh_off, (const bf16_t*)Wout, Cout, p, h, w, out);
+    else
+        hipLaunchKernelGGL(k_prefinal_project<float>, dim3(blocks), dim3(256), 0, s, resid, g, d, mod,
+                           mod_stride, sc_off, sh_off, (const float*)Wout, Cout, p, h, w, out);
+    return hipGetLastError();
+}
+
+// ============================================================================ Euler + CFG
+// [PIPE] AuraFlowPipeline 核心参数详解 / [TRANS] 在 AuraFlowPipeline 中的实际调用:
+// v_hat = v_u + s (v_c - v_u) with v = [uncond; cond] when CFG is on, else v;
+// x <- x + (sigma_next - sigma) v_hat.
+__global__ void k_euler_cfg(float* __restrict__ x, const float* __restrict__ v, long n, float dt, float gs,
+                            int cfg_on) {
+    long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    float vh;
+    if (cfg_on) {
+        float vu = v[i], vc = v[n + i];
+        vh = vu + gs * (vc - vu);
+    } else {
+        vh = v[i];
+    }
+    x[i] = x[i] + dt * vh;
+}
+
+hipError_t euler_cfg(float* x, const float* v, long n, float dt, float guidance, int cfg_on, hipStream_t s) {
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_euler_cfg, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, x, v, n, dt, guidance,
+                       cfg_on);
+    return hipGetLastError();
+}
+
+// ============================================================================ weight packing
+// Canonical fp32 tensors -> device layout. FFN gate/up rows are interleaved in
+// 32-row groups ([F, d] gate rows f -> packed row (f/32)*64 + f%32, up rows ->
+// (f/32)*64 + 32 + f%32) so that a 64-column GEMM tile holds matching gate and
+// up columns in the same lane.
+__global__ void k_pack(const float* __restrict__ src, long n, long first, void* __restrict__ dst, int to_bf16,
+                       int layout, int cols) {
+    long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    long e = first + i;
+    long o = e;
+    if (layout != PACK_PLAIN) {
+        long f = e / cols, c = e % cols;
+        long prow = (f / 32) * 64 + (layout == PACK_FFN_UP ? 32 : 0) + f % 32;
+        o = prow * cols + c;
+    }
+    if (to_bf16) ((bf16_t*)dst)[o] = f2bf(src[i]);
+    else ((float*)dst)[o] = src[i];
+}
+
+hipError_t pack_weights(const float* src, long n, long first, void* dst, af_dtype ddt, int layout, int cols,
+                        hipStream_t s) {
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_pack, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, src, n, first, dst,
+                       ddt == AF_BF16 ? 1 : 0, layout, cols);
+    return hipGetLastError();
+}
+
+// ============================================================================ residual -> [B, S, d]
+__global__ void k_taps(const float* __restrict__ resid, RowGeom g, int d, float* __restrict__ out) {
+    long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    long n = (long)g.B * g.S() * d;
+    if (i >= n) return;
+    int c = i % d;
+    long bs = i / d;
+    int s_ = bs % g.S(), b = bs / g.S();
+    out[i] = resid[(long)g.row_of(b, s_) * d + c];
+}
+
+hipError_t taps_permute(const float* resid, RowGeom g, int d, float* out, hipStream_t s) {
+    long n = (long)g.B * g.S() * d;
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_taps, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, resid, g, d, out);
+    return hipGetLastError();
+}
+
+// ============================================================================ fp32 path helpers
+// raw [M, 3d] = [q | k | v]; q and k get a per-head LayerNorm over hd (QK-norm,
+// [TRANS] 注意力处理器与 QKV 融合), all three are scattered to [B, H, S_pad, hd].
+__global__ void k_qknorm_scatter_f32(const float* __restrict__ raw, int M, RowGeom g, int H, int hd, int S_pad,
+                                     float eps, float* __restrict__ q, float* __restrict__ k,
+                                     float* __restrict__ v, int row0) {
+    long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (long)M * H * 3) return;
+    int which = i % 3;
+    int h = (i / 3) % H;
+    int m = i / (3 * H);
+    int d = H * hd;
+    int r = row0 + m;
+    int b = g.batch_of(r), s_ = g.seq_of(r);
+    const float* src = raw + (long)m * 3 * d + which * d + h * hd;
+    float* dst = (which == 0 ? q : which == 1 ? k : v) + (((long)b * H + h) * S_pad + s_) * hd;
+    if (which == 2) {
+        for (int t = 0; t < hd; ++t) dst[t] = src[t];
+        return;
+    }
+    float mean = 0.f;
+    for (int t = 0; t < hd; ++t) mean += src[t];
+    mean /= (float)hd;
+    float var = 0.f;
+    for (int t = 0; t < hd; ++t) { float c = src[t] - mean; var += c * c; }
+    float rstd = rsqrtf(var / (float)hd + eps);
+    for (int t = 0; t < hd; ++t) dst[t] = (src[t] - mean) * rstd;
+}
+
+hipError_t qknorm_scatter_f32(const float* raw, int M, RowGeom g, int H, int hd, int S_pad, float eps, float* q,
+                              float* k, float* v, int row0, hipStream_t s) {
+    long n = (long)M * H * 3;
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_qknorm_scatter_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, raw, M, g, H, hd,
+                       S_pad, eps, q, k, v, row0);
+    return hipGetLastError();
+}
+
+// raw [M, 2F] in the 32-column gate/up interleave -> h[m, f] = silu(gate) * up.
+__global__ void k_swiglu_f32(const float* __restrict__ raw, int M, int F, float* __restrict__ h) {
+    long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (long)M * F) return;
+    int f = i % F;
+    long m = i / F;
+    long base = m * 2 * F + (f / 32) * 64 + f % 32;
+    float a = raw[base], u = raw[base + 32];
+    h[i] = silu_f(a) * u;
+}
+
+hipError_t swiglu_f32(const float* raw, int M, int F, float* h, hipStream_t s) {
+    long n = (long)M * F;
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_swiglu_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, raw, M, F, h);
+    return hipGetLastError();
+}
+
+}  // namespace af

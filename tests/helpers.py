@@ -1,0 +1,60 @@
+"""Shared helpers for the GPU parity tests: config translation, seeded inputs,
+comparison metrics. No model arithmetic lives here."""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+import seeded_inputs
+
+
+def oracle_cfg(c) -> oracle.AuraFlowConfig:
+    """The oracle's config with the same sizes as a library AfConfig."""
+    return oracle.AuraFlowConfig(
+        in_channels=c.in_channels, out_channels=c.out_channels, patch_size=c.patch_size,
+        num_mmdit_layers=c.num_mmdit_layers, num_single_dit_layers=c.num_single_dit_layers,
+        num_attention_heads=c.num_attention_heads, attention_head_dim=c.attention_head_dim,
+        joint_attention_dim=c.joint_attention_dim, caption_projection_dim=c.caption_projection_dim,
+        pos_embed_max_size=c.pos_embed_max_size, num_register_tokens=c.num_register_tokens,
+        ln_eps=float(np.float32(c.ln_eps)), timestep_scale=float(c.timestep_scale))
+
+
+def workload_inputs(B, C, H, W, T, Dtxt, lengths=None, cfg_pairs=True, tau=None):
+    """Seeded inputs in the shape of the pages' workloads.
+
+    cfg_pairs: the batch is [uncond; cond] halves sharing one latent per image
+    (latents duplicated for CFG) and one timestep; text drawn independently per
+    row. lengths: per-row valid text lengths (None = all valid).
+    """
+    if cfg_pairs:
+        assert B % 2 == 0
+        half = seeded_inputs.latents(B // 2, C, H, W)
+        lat = np.concatenate([half, half])
+        t = seeded_inputs.timesteps_uniform(B // 2) if tau is None else None
+        taus = np.concatenate([t, t]) / 1000.0 if tau is None else np.full(B, tau)
+    else:
+        lat = seeded_inputs.latents(B, C, H, W)
+        taus = seeded_inputs.timesteps_uniform(B) / 1000.0 if tau is None else np.full(B, tau)
+    text = seeded_inputs.text_embeddings(B, T, Dtxt)
+    mask = None if lengths is None else seeded_inputs.length_mask(np.asarray(lengths), T)
+    return lat, taus.astype(np.float32), text, mask
+
+
+def rel_max(a, ref):
+    a = np.asarray(a, np.float64)
+    ref = np.asarray(ref, np.float64)
+    return float(np.abs(a - ref).max() / np.abs(ref).max())
+
+
+def cosine(a, ref):
+    a = np.asarray(a, np.float64).ravel()
+    ref = np.asarray(ref, np.float64).ravel()
+    return float(a @ ref / (np.linalg.norm(a) * np.linalg.norm(ref)))
+
+
+def to_dev(x, dtype=None):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x))
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.cuda()

@@ -1,0 +1,145 @@
+"""Host-side checks of the C-ABI library (no GPU): exported symbols, input
+validation, the canonical weight list and the sigma schedule."""
+import ctypes
+import json
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "auraflow.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(af_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol(af):
+    lib = ctypes.CDLL(af._LIB_PATH)
+    names = _declared()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(af.EXPORTED) == names
+
+
+def _cfg(af, **kw):
+    return af.make_config(**kw)
+
+
+def test_default_config_matches_pages(af):
+    c = af.af_config_default()
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "auraflow_config.json")))["default"]
+    for k in ("patch_size", "in_channels", "out_channels", "num_mmdit_layers", "num_single_dit_layers",
+              "attention_head_dim", "num_attention_heads", "joint_attention_dim", "caption_projection_dim"):
+        assert getattr(c, k) == g[k], k
+    assert c.pos_embed_max_size == 96 * 96 and c.num_register_tokens == 8
+
+
+@pytest.mark.parametrize("B,H,W,T,ok", [
+    (2, 128, 128, 256, True), (0, 128, 128, 256, True), (2, 128, 128, 0, True), (1, 2, 2, 1, True),
+    (2, 127, 128, 256, False), (2, 128, 129, 256, False), (3, 128, 128, 256, False),
+    (2, 128, 128, 257, False), (2, 130, 128, 256, False), (-1, 128, 128, 1, False),
+])
+def test_check_shapes(af, B, H, W, T, ok):
+    c = _cfg(af)
+    if ok:
+        af.af_check_shapes(c, B, H, W, T)
+    else:
+        with pytest.raises(ValueError):
+            af.af_check_shapes(c, B, H, W, T)
+
+
+def test_check_shapes_grid_limit(af):
+    c = _cfg(af, max_latent_h=256, max_latent_w=256)
+    af.af_check_shapes(c, 1, 192, 192, 8)                  # 96 x 96 uses the whole PE grid
+    with pytest.raises(ValueError, match="position"):
+        af.af_check_shapes(c, 1, 194, 64, 8)               # 97 rows of patches > 96
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("caption_projection_dim", 2048, 2), ("pos_embed_max_size", 9000, 2), ("attention_head_dim", 128, 3),
+    ("compute_dtype", 7, 1), ("num_attention_heads", 0, 1), ("ln_eps", 0.0, 1),
+])
+def test_config_errors(af, field, value, status):
+    c = _cfg(af, **{field: value})
+    if field == "attention_head_dim":
+        c.caption_projection_dim = c.num_attention_heads * value
+    with pytest.raises(ValueError) as e:
+        af.af_check_shapes(c, 1, 64, 64, 8)
+    assert e.value.status == status
+    assert af._lib.af_last_error().decode() != ""
+
+
+def test_fp32_path_limits(af):
+    c = _cfg(af, compute_dtype=af.AF_F32, num_attention_heads=4, attention_head_dim=8,
+             caption_projection_dim=32, joint_attention_dim=32, pos_embed_max_size=64)
+    af.af_check_shapes(c, 1, 16, 16, 8)
+    c.attention_head_dim, c.caption_projection_dim = 128, 512
+    with pytest.raises(ValueError):
+        af.af_check_shapes(c, 1, 16, 16, 8)
+
+
+def _oracle_cfg(c):
+    return oracle.AuraFlowConfig(
+        in_channels=c.in_channels, out_channels=c.out_channels, patch_size=c.patch_size,
+        num_mmdit_layers=c.num_mmdit_layers, num_single_dit_layers=c.num_single_dit_layers,
+        num_attention_heads=c.num_attention_heads, attention_head_dim=c.attention_head_dim,
+        joint_attention_dim=c.joint_attention_dim, caption_projection_dim=c.caption_projection_dim,
+        pos_embed_max_size=c.pos_embed_max_size, num_register_tokens=c.num_register_tokens)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(),
+    dict(num_mmdit_layers=1, num_single_dit_layers=1),
+    dict(compute_dtype=0, num_attention_heads=4, attention_head_dim=8, caption_projection_dim=32,
+         joint_attention_dim=32, pos_embed_max_size=64, num_mmdit_layers=1, num_single_dit_layers=1),
+])
+def test_weight_list_matches_oracle_list(af, kw):
+    c = _cfg(af, **kw)
+    n, total = af.af_weight_count(c)
+    specs = oracle.weight_specs(_oracle_cfg(c))
+    assert n == len(specs)
+    off = 0
+    for i, (name, shape, _std) in enumerate(specs):
+        lname, rows, cols, loff = af.af_weight_info(c, i)
+        assert lname == name
+        assert (rows, cols) == (shape[0], shape[1] if len(shape) > 1 else 1)
+        assert loff == off
+        off += int(np.prod(shape))
+    assert total == off == oracle.count_parameters(_oracle_cfg(c))
+    # The synthetic init scale is part of the input recipe; both sides agree on it.
+    for name, _shape, std in specs:
+        assert af.weight_std(name) == std
+
+
+def test_sigma_schedule_library(af):
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "sigma_schedule.json")))
+    s = af.af_sigma_schedule(4, 1.73)
+    assert s[0] == 1.0 and s[-1] == 0.0
+    assert abs(s[2] - g["sigma_at_u"]["0.5"]) < 1e-7 and abs(s[3] - g["sigma_at_u"]["0.25"]) < 1e-7
+    np.testing.assert_allclose(af.af_sigma_schedule(25, 1.73), oracle.sigma_schedule(25, 1.73), atol=1e-7)
+    with pytest.raises(ValueError):
+        af.af_sigma_schedule(0, 1.73)
+    with pytest.raises(ValueError):
+        af.af_sigma_schedule(5, -1.0)
+
+
+def test_euler_step_argument_errors_without_device(af):
+    lib = af._lib
+    assert lib.af_flow_euler_cfg_step(None, None, 0, 4, 8, 8, 1.0, 0.5, 3.5, None) == af.AF_OK   # empty
+    assert lib.af_flow_euler_cfg_step(None, None, -1, 4, 8, 8, 1.0, 0.5, 3.5, None) == af.AF_E_INVALID_ARG
+    assert lib.af_flow_euler_cfg_step(None, None, 1, 4, 8, 8, 1.0, 0.5, 3.5, None) == af.AF_E_INVALID_ARG
+    assert lib.af_status_string(af.AF_E_SHAPE) == b"shape error"
+
+
+def test_forward_rejects_null_model(af):
+    lib = af._lib
+    st = lib.af_transformer_forward(None, None, None, None, 0, None, 1, 16, 16, 8, None, None)
+    assert st == af.AF_E_INVALID_ARG
+    assert b"model" in lib.af_last_error()
