@@ -504,9 +504,13 @@ af_status run_forward(af_model* m, const Inputs& in, int stop_after, float* resi
     AF_K(patch_embed(in.latents, c.in_channels, in.H, in.W, p, m->pe_w, m->pe_b, m->dt, m->pos, D.G, m->resid, g, d, s));
     AF_K(copy_registers(m->reg, m->dt, D.R, m->resid, g, d, s));
     if (in.T > 0) {
+        // bf16 path: text is staged in the padded internal buffer (rounded to bf16
+        // when it arrives as fp32).
         const void* text = in.text;
-        if (m->dt == AF_BF16 && in.text_dtype == AF_F32) {
-            AF_K(f32_to_bf16((const float*)in.text, m->text_bf16, (long)in.B * in.T * c.joint_attention_dim, s));
+        if (m->dt == AF_BF16) {
+            const long n = (long)in.B * in.T * c.joint_attention_dim;
+            if (in.text_dtype == AF_F32) AF_K(f32_to_bf16((const float*)in.text, m->text_bf16, n, s));
+            else AF_K(hipMemcpyAsync(m->text_bf16, in.text, (size_t)n * 2, hipMemcpyDeviceToDevice, s));
             text = m->text_bf16;
         }
         GemmLaunch L = gemm_base(m, g, d, c.joint_attention_dim, EPI_STORE_MAPPED);
@@ -671,11 +675,15 @@ af_status af_create(const af_config* c, int device, af_model** out) {
     const long Bm = c->max_batch > 0 ? c->max_batch : 1;
     const long Mm = m->M_max > 0 ? m->M_max : 1;
     const long d = D.d, F = D.F;
+    // GEMM A operands (nrm, attn, ffh, text) carry one 256-row tile of padding:
+    // tail tiles of the bf16 GEMM read past the last row and discard the results.
+    const long Mp = Mm + 256;
+    const long Tp = Bm * (long)(c->max_text_len > 0 ? c->max_text_len : 1) + 256;
     std::vector<std::pair<void**, size_t>> ws = {
         {(void**)&m->resid, Mm * d * 4},
-        {&m->nrm, Mm * d * m->es},
-        {&m->attn, Mm * d * m->es},
-        {&m->ffh, Mm * F * m->es},
+        {&m->nrm, Mp * d * m->es},
+        {&m->attn, Mp * d * m->es},
+        {&m->ffh, Mp * F * m->es},
         {&m->q, Bm * D.H * (size_t)m->S_pad_max * D.hd * m->es},
         {&m->k, Bm * D.H * (size_t)m->S_pad_max * D.hd * m->es},
         {&m->v, Bm * D.H * (size_t)m->S_pad_max * D.hd * m->es},
@@ -684,7 +692,7 @@ af_status af_create(const af_config* c, int device, af_model** out) {
         {(void**)&m->hpre, Bm * d * 4},
         {(void**)&m->tfeat, Bm * 256 * 4},
         {(void**)&m->kbias, Bm * (size_t)m->S_pad_max * 4},
-        {(void**)&m->text_bf16, Bm * (size_t)(c->max_text_len > 0 ? c->max_text_len : 1) * c->joint_attention_dim * 2},
+        {(void**)&m->text_bf16, (size_t)Tp * c->joint_attention_dim * 2},
     };
     if (m->dt == AF_F32) ws.push_back({(void**)&m->raw, Mm * std::max(3 * d, 2 * F) * 4});
     m->staging_floats = 16u << 20;

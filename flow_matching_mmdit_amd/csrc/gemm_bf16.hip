@@ -13,36 +13,81 @@
 //
 // Tiling: 256 x 256 block tile, BK = 64, four waves in a 2 x 2 arrangement, each
 // wave owning a 128 x 128 sub-tile (4 x 4 MFMA tiles, 256 fp32 accumulators per
-// lane). A and W tiles are staged through LDS with two stages (128 KB); 16-byte
-// chunks are XOR-swizzled by row so the MFMA operand reads are bank-conflict
-// free. Up to two row groups with different weights share one launch (the joint
-// blocks' text and image streams).
+// lane, held in AGPRs). A and W tiles move global -> LDS with the gfx950 direct
+// loads (global_load_lds_dwordx4: lane i writes LDS bytes [16 i, 16 i + 16) of
+// the instruction's 1 KB block), two stages; the XOR swizzle of 16-byte chunks
+// is applied by choosing which global chunk each lane fetches, so the MFMA
+// operand reads (ds_read_b128) are bank-conflict free. Blocks are mapped to
+// tiles XCD by XCD (consecutive block ids go to different XCDs) and, inside an
+// XCD, in groups of four tile rows so co-resident blocks share A and W panels in
+// that XCD's L2. Up to two row groups with different weights share one launch
+// (the joint blocks' text and image streams). Epilogues that write bf16 stage
+// the tile in LDS and store 16-byte chunks.
 #include "af_internal.h"
 
 namespace af {
 
 namespace {
 constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int TILE_ELEMS = BM * BK;  // bf16 elements of one staged A (or W) tile
+constexpr int TILE_ELEMS = BM * BK;  // bf16 elements of one staged A (or W) tile (32 KB)
+constexpr int NXCD = 8;              // MI355X: 8 XCDs, blocks dispatched round-robin
+constexpr int GROUP_M = 4;
+constexpr int QS = 264;              // QKV epilogue staging row stride (elements)
+constexpr int HS = 136;              // SwiGLU epilogue staging row stride (elements)
+constexpr int SMEM_ELEMS = 256 * QS + 2048;   // >= 4 tiles; + [2][256] x 2 fp32 row statistics
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void glb_void;
 
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+__host__ __device__ __forceinline__ int tiles_m(int M) { return (M + BM - 1) / BM; }
 
-__device__ __forceinline__ int tiles_m(int M) { return (M + BM - 1) / BM; }
+// Issues this wave's share (8 x 1 KB) of one 256 x 64 tile starting at `tile`
+// (uniform): instruction j covers tile rows [8 cb, 8 cb + 8), cb = wave * 8 + j;
+// lane l fills physical chunk l & 7 of row 8 cb + (l >> 3) with logical chunk
+// (l & 7) ^ swz(row). swz alternates with the parity of cb only, so two per-lane
+// offsets (off[j & 1]) plus a uniform row step cover all eight instructions.
+__device__ __forceinline__ void issue_tile(const bf16_t* tile, const uint32_t* off, long ld, bf16_t* lds_tile,
+                                           int wave) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const bf16_t* src = tile + (long)(j & ~1) * 8 * ld + off[j & 1];
+        __builtin_amdgcn_global_load_lds((glb_void*)src, (lds_void*)(lds_tile + (wave * 8 + j) * 512), 16, 0, 0);
+    }
+}
 }  // namespace
 
 template <int EPI>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_gemm_bf16(GemmLaunch L) {
-    __shared__ __attribute__((aligned(16))) bf16_t smem[2 * 2 * TILE_ELEMS];
+    static_assert(SMEM_ELEMS >= 4 * TILE_ELEMS, "LDS");
+    __shared__ __attribute__((aligned(1024))) bf16_t smem[SMEM_ELEMS];
+    bf16_t* const sA0 = smem;
+    bf16_t* const sW0 = smem + TILE_ELEMS;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const int tiles_n = L.N / BN;
 
-    int bid = blockIdx.x;
-    const int t0 = tiles_m(L.g[0].M) * tiles_n;
-    const int gi = bid >= t0 ? 1 : 0;
-    if (gi) bid -= t0;
+    // ---- block -> (group, tile row, tile column)
+    const int tm0 = tiles_m(L.g[0].M), tm1 = L.ngroups > 1 ? tiles_m(L.g[1].M) : 0;
+    const int T0 = tm0 * tiles_n, T = T0 + tm1 * tiles_n;
+    int lid;
+    {
+        const int b = blockIdx.x, x = b % NXCD, q = T / NXCD, r = T % NXCD;
+        lid = x * q + min(x, r) + b / NXCD;
+    }
+    const int gi = lid >= T0 ? 1 : 0;
+    if (gi) lid -= T0;
+    const int tmg = gi ? tm1 : tm0;
+    int tm, tn;
+    {
+        const int per = GROUP_M * tiles_n;
+        const int gblk = lid / per, idx = lid % per;
+        const int gm = min(GROUP_M, tmg - gblk * GROUP_M);
+        tm = gblk * GROUP_M + idx % gm;
+        tn = idx / gm;
+    }
     const bf16_t* __restrict__ A = (const bf16_t*)(gi ? L.g[1].A : L.g[0].A);
     const long lda = gi ? L.g[1].lda : L.g[0].lda;
     const bf16_t* __restrict__ W = (const bf16_t*)(gi ? L.g[1].W : L.g[0].W);
@@ -50,32 +95,22 @@ void k_gemm_bf16(GemmLaunch L) {
     const int M = gi ? L.g[1].M : L.g[0].M;
     const int row0 = gi ? L.g[1].row0 : L.g[0].row0;
     const int gate_off = gi ? L.g[1].gate_off : L.g[0].gate_off;
-
-    const int tn = bid % tiles_n, tm = bid / tiles_n;
     const int m0 = tm * BM, n0 = tn * BN;
     const int K = L.K;
 
-    uint4 ra[8], rb[8];
-    auto gload = [&](int k0) {
+    // Per-lane element offsets for the direct loads (logical chunk folded in). Rows
+    // past M read the padding rows every activation buffer carries (at least one
+    // tile of rows past its last real row); their results are never stored.
+    uint32_t aoff[2], woff[2];
 #pragma unroll
-        for (int p = 0; p < 8; ++p) {
-            int r = p * 32 + (tid >> 3);
-            int gr = min(m0 + r, M - 1);
-            ra[p] = *reinterpret_cast<const uint4*>(A + (long)gr * lda + k0 + (tid & 7) * 8);
-            rb[p] = *reinterpret_cast<const uint4*>(W + (long)(n0 + r) * ldw + k0 + (tid & 7) * 8);
-        }
-    };
-    auto sstore = [&](int stage) {
-        bf16_t* sA = smem + stage * 2 * TILE_ELEMS;
-        bf16_t* sB = sA + TILE_ELEMS;
-#pragma unroll
-        for (int p = 0; p < 8; ++p) {
-            int r = p * 32 + (tid >> 3);
-            int c = (tid & 7) ^ swz(r);
-            *reinterpret_cast<uint4*>(sA + r * BK + c * 8) = ra[p];
-            *reinterpret_cast<uint4*>(sB + r * BK + c * 8) = rb[p];
-        }
-    };
+    for (int j = 0; j < 2; ++j) {
+        const int r = (wave * 8 + j) * 8 + (lane >> 3);
+        const int c = (lane & 7) ^ swz(r);
+        aoff[j] = (uint32_t)(r * lda + c * 8);
+        woff[j] = (uint32_t)(r * ldw + c * 8);
+    }
+    const bf16_t* Atile = A + (long)m0 * lda;
+    const bf16_t* Wtile = W + (long)n0 * ldw;
 
     f32x16 acc[4][4];
 #pragma unroll
@@ -85,46 +120,62 @@ void k_gemm_bf16(GemmLaunch L) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    auto compute = [&](int stage) {
-        const bf16_t* sA = smem + stage * 2 * TILE_ELEMS;
-        const bf16_t* sB = sA + TILE_ELEMS;
+    // MFMA operands for k-step ks come from LDS one step ahead (register double
+    // buffer), so the reads of step ks + 1 overlap the MFMAs of step ks.
+    auto load_frags = [&](const bf16_t* sA, const bf16_t* sB, int ks, bf16x8* a, bf16x8* b) {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            int r = wm * 128 + mt * 32 + (lane & 31);
+            int c = (ks * 2 + (lane >> 5)) ^ swz(r);
+            a[mt] = *reinterpret_cast<const bf16x8*>(sA + r * BK + c * 8);
+        }
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+            int r = wn * 128 + nt * 32 + (lane & 31);
+            int c = (ks * 2 + (lane >> 5)) ^ swz(r);
+            b[nt] = *reinterpret_cast<const bf16x8*>(sB + r * BK + c * 8);
+        }
+    };
+    auto compute = [&](const bf16_t* sA, const bf16_t* sB) {
+        bf16x8 a[2][4], b[2][4];
+        load_frags(sA, sB, 0, a[0], b[0]);
 #pragma unroll
         for (int ks = 0; ks < BK / 16; ++ks) {
-            bf16x8 a[4], b[4];
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                int r = wm * 128 + mt * 32 + (lane & 31);
-                int c = (ks * 2 + (lane >> 5)) ^ swz(r);
-                a[mt] = *reinterpret_cast<const bf16x8*>(sA + r * BK + c * 8);
-            }
-#pragma unroll
-            for (int nt = 0; nt < 4; ++nt) {
-                int r = wn * 128 + nt * 32 + (lane & 31);
-                int c = (ks * 2 + (lane >> 5)) ^ swz(r);
-                b[nt] = *reinterpret_cast<const bf16x8*>(sB + r * BK + c * 8);
-            }
+            if (ks + 1 < BK / 16) load_frags(sA, sB, ks + 1, a[(ks + 1) & 1], b[(ks + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);   // keep the reads of step ks + 1 ahead of these MFMAs
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
                 for (int nt = 0; nt < 4; ++nt)
-                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mt], b[nt], acc[mt][nt], 0, 0, 0);
+                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks & 1][mt], b[ks & 1][nt], acc[mt][nt],
+                                                                          0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
 
+    // ---- main loop: two LDS stages. Tile kt + 1 streams into the idle stage
+    // while tile kt is multiplied; the wait + barrier at the end of the
+    // iteration makes it visible to every wave before it is read.
     const int KT = K / BK;
-    gload(0);
-    sstore(0);
+    issue_tile(Atile, aoff, lda, sA0, wave);
+    issue_tile(Wtile, woff, ldw, sW0, wave);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int kt = 0; kt < KT; ++kt) {
-        if (kt + 1 < KT) gload((kt + 1) * BK);
-        compute(kt & 1);
-        if (kt + 1 < KT) sstore((kt + 1) & 1);
+        const int cur = (kt & 1) * 2 * TILE_ELEMS;
+        if (kt + 1 < KT) {
+            const int nxt = 2 * TILE_ELEMS - cur;
+            issue_tile(Atile + (kt + 1) * BK, aoff, lda, smem + nxt, wave);
+            issue_tile(Wtile + (kt + 1) * BK, woff, ldw, smem + nxt + TILE_ELEMS, wave);
+        }
+        compute(smem + cur, smem + cur + TILE_ELEMS);
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
 
     // ---------------------------------------------------------------- epilogues
     // acc[mt][nt][i*4+j] holds row wm*128 + mt*32 + i*8 + (lane>>5)*4 + j,
-    // column wn*128 + nt*32 + (lane&31) of the block tile.
+    // column wn*128 + nt*32 + (lane&31) of the block tile. LDS is free here.
     const int lr_base = wm * 128 + (lane >> 5) * 4;
     const int lc_base = wn * 128 + (lane & 31);
 
@@ -167,30 +218,43 @@ void k_gemm_bf16(GemmLaunch L) {
                 }
             }
     } else if constexpr (EPI == EPI_SWIGLU) {
-        bf16_t* Hout = (bf16_t*)L.C;
+        // h tile [256 rows][128 cols] bf16 staged in LDS, then 16-byte row stores.
+        bf16_t* st = smem;
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                int m = m0 + lr_base + mt * 32 + (r >> 2) * 8 + (r & 3);
-                if (m >= M) continue;
+                int lr = lr_base + mt * 32 + (r >> 2) * 8 + (r & 3);
 #pragma unroll
                 for (int p2 = 0; p2 < 2; ++p2) {
                     float gt = acc[mt][2 * p2][r], up = acc[mt][2 * p2 + 1][r];
-                    int f = (n0 + wn * 128 + p2 * 64) / 2 + (lane & 31);
-                    Hout[(long)(row0 + m) * L.ldc + f] = f2bf(silu_f(gt) * up);
+                    st[lr * HS + wn * 64 + p2 * 32 + (lane & 31)] = f2bf(silu_f(gt) * up);
                 }
             }
+        __syncthreads();
+        bf16_t* Hout = (bf16_t*)L.C;
+        const int fcol0 = n0 / 2;
+#pragma unroll 4
+        for (int it = 0; it < 16; ++it) {
+            int idx = it * 256 + tid;          // 256 rows x 16 chunks
+            int lr = idx >> 4, ch = idx & 15;
+            int m = m0 + lr;
+            if (m < M) {
+                uint4 v = *reinterpret_cast<const uint4*>(st + lr * HS + ch * 8);
+                *reinterpret_cast<uint4*>(Hout + (long)(row0 + m) * L.ldc + fcol0 + ch * 8) = v;
+            }
+        }
     } else if constexpr (EPI == EPI_QKV) {
         const int dmodel = L.N / 3;
         const int which = n0 / dmodel;          // 0 q, 1 k, 2 v
         const int head = (n0 % dmodel) / BN;    // one block tile = one 256-wide head
         const int H = L.H, S_pad = L.S_pad;
+        // Output tile [256 rows][256 cols] bf16 staged in LDS (row stride QS).
+        bf16_t* st = smem;
+        float* rsum = reinterpret_cast<float*>(smem + 256 * QS);   // [2][256]
+        float* rsq = rsum + 512;                                    // [2][256]
         if (which < 2) {
-            // Per-row LayerNorm over the 256 head columns, split across the two wn
-            // waves; row statistics live in LDS (free after the main loop).
-            float* rsum = reinterpret_cast<float*>(smem);   // [2][256] partial sums
-            float* rsq = rsum + 512;                         // [2][256] partial centred squares
+            // Per-row LayerNorm over the 256 head columns, split across the two wn waves.
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -216,53 +280,87 @@ void k_gemm_bf16(GemmLaunch L) {
                     if ((lane & 31) == 0) rsq[wn * 256 + lr] = s;
                 }
             __syncthreads();
-            bf16_t* dst = (bf16_t*)(which == 0 ? L.q : L.k);
-#pragma unroll 1
+#pragma unroll
             for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     int lr = lr_base + mt * 32 + (r >> 2) * 8 + (r & 3);
-                    int m = m0 + lr;
-                    if (m >= M) continue;
                     float mean = (rsum[lr] + rsum[256 + lr]) * (1.f / 256.f);
                     float rstd = rsqrtf((rsq[lr] + rsq[256 + lr]) * (1.f / 256.f) + L.eps);
-                    int rr = row0 + m;
-                    int b = L.geom.batch_of(rr), s_ = L.geom.seq_of(rr);
-                    bf16_t* drow = dst + (((long)b * H + head) * S_pad + s_) * 256;
 #pragma unroll
                     for (int nt = 0; nt < 4; ++nt)
-                        drow[lc_base + nt * 32] = f2bf((acc[mt][nt][r] - mean) * rstd);
+                        st[lr * QS + lc_base + nt * 32] = f2bf((acc[mt][nt][r] - mean) * rstd);
                 }
+            __syncthreads();
+            // rows -> [B, H, S_pad, 256]: 32 chunks of 16 B per row
+            bf16_t* dst = (bf16_t*)(which == 0 ? L.q : L.k);
+#pragma unroll 4
+            for (int it = 0; it < 32; ++it) {
+                int idx = it * 256 + tid;
+                int lr = idx >> 5, ch = idx & 31;
+                int m = m0 + lr;
+                if (m < M) {
+                    int rr = row0 + m;
+                    int b = L.geom.batch_of(rr), s_ = L.geom.seq_of(rr);
+                    uint4 v = *reinterpret_cast<const uint4*>(st + lr * QS + ch * 8);
+                    *reinterpret_cast<uint4*>(dst + (((long)b * H + head) * S_pad + s_) * 256 + ch * 8) = v;
+                }
+            }
         } else {
-            bf16_t* vt = (bf16_t*)L.vt;
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    int m = m0 + lr_base + mt * 32 + (r >> 2) * 8 + (r & 3);
-                    if (m >= M) continue;
-                    int rr = row0 + m;
-                    int b = L.geom.batch_of(rr), s_ = L.geom.seq_of(rr);
-                    bf16_t* base = vt + ((long)b * H + head) * 256 * (long)S_pad + s_;
+                    int lr = lr_base + mt * 32 + (r >> 2) * 8 + (r & 3);
 #pragma unroll
-                    for (int nt = 0; nt < 4; ++nt)
-                        base[(long)(lc_base + nt * 32) * S_pad] = f2bf(acc[mt][nt][r]);
+                    for (int nt = 0; nt < 4; ++nt) st[lr * QS + lc_base + nt * 32] = f2bf(acc[mt][nt][r]);
                 }
+            __syncthreads();
+            // v^T: for head column c, 8 consecutive tile rows -> 8 consecutive keys (one
+            // 16-byte store) when they lie in one sample's segment and start 8-aligned;
+            // otherwise element stores.
+            bf16_t* vt = (bf16_t*)L.vt;
+#pragma unroll 2
+            for (int it = 0; it < 32; ++it) {
+                int idx = it * 256 + tid;              // 256 columns x 32 row-chunks
+                int c = idx & 255, rc = idx >> 8;
+                int lr0 = rc * 8;
+                int m = m0 + lr0;
+                if (m >= M) continue;
+                int rr = row0 + m;
+                int b = L.geom.batch_of(rr), s0 = L.geom.seq_of(rr);
+                bool fast = (m + 7 < M) && (s0 % 8 == 0) && L.geom.batch_of(rr + 7) == b &&
+                            L.geom.seq_of(rr + 7) == s0 + 7;
+                if (fast) {
+                    uint32_t w[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        w[e] = (uint32_t)st[(lr0 + 2 * e) * QS + c] | ((uint32_t)st[(lr0 + 2 * e + 1) * QS + c] << 16);
+                    bf16_t* base = vt + (((long)b * H + head) * 256 + c) * (long)S_pad;
+                    *reinterpret_cast<uint4*>(base + s0) = make_uint4(w[0], w[1], w[2], w[3]);
+                } else {
+                    for (int e = 0; e < 8 && m + e < M; ++e) {
+                        int re = rr + e;
+                        int be = L.geom.batch_of(re), se = L.geom.seq_of(re);
+                        vt[(((long)be * H + head) * 256 + c) * (long)S_pad + se] = st[(lr0 + e) * QS + c];
+                    }
+                }
+            }
         }
     }
 }
 
 hipError_t gemm_bf16(const GemmLaunch& L, hipStream_t s) {
     int tiles_n = L.N / BN;
-    int total = 0;
-    for (int i = 0; i < L.ngroups; ++i) total += ((L.g[i].M + BM - 1) / BM) * tiles_n;
-    if (total == 0) return hipSuccess;
     GemmLaunch LL = L;
-    if (LL.ngroups < 2) LL.g[1] = LL.g[0], LL.g[1].M = 0;
-    if (LL.g[0].M == 0) {  // keep group 0 non-empty so the tile split is simple
+    if (LL.ngroups == 2 && LL.g[0].M == 0) {  // keep group 0 non-empty
         LL.g[0] = LL.g[1];
-        LL.g[1].M = 0;
+        LL.ngroups = 1;
     }
+    if (LL.ngroups == 2 && LL.g[1].M == 0) LL.ngroups = 1;
+    int total = 0;
+    for (int i = 0; i < LL.ngroups; ++i) total += tiles_m(LL.g[i].M) * tiles_n;
+    if (total == 0) return hipSuccess;
     dim3 grid(total), block(256);
     switch (L.epi) {
         case EPI_STORE: hipLaunchKernelGGL(k_gemm_bf16<EPI_STORE>, grid, block, 0, s, LL); break;
