@@ -9,16 +9,26 @@
 // the QKV GEMM epilogue so the P V contraction reads keys contiguously);
 // output o [M, d] in residual-row order.
 //
-// One workgroup = 4 waves = 128 queries of one (b, h); each wave owns 32 queries.
-// Per 64-key tile:
-//   S^T = K Q^T  (A = K from LDS, B = the wave's Q held in registers)
-//     -> the accumulator has one query per lane (lane & 31) and 32 keys per lane,
-//        so row max / row sum need one cross-half-wave exchange;
-//   O^T += V^T P^T (A = v^T from LDS, B = P taken straight from the S^T
-//     accumulator registers; the key order inside each 16-key MFMA step is
-//     permuted identically on both operands, so P never goes through LDS).
-// Online softmax keeps (m, l) per query in fp32; exp via exp2 with log2(e)
-// folded into the scale.
+// One workgroup = 4 waves = 128 queries of one (b, h); each wave owns 32 queries
+// and keeps them in registers as MFMA B operands. Per 64-key tile:
+//   S^T = K Q^T  (A = K rows from LDS) -> one query per lane (lane & 31),
+//   P = exp2(S^T * log2(e)/16 - ref + bias),
+//   O^T += V^T P^T (A = v^T from LDS, B = P straight from the S^T registers).
+// The K rows each lane feeds to the S^T MFMA are permuted (bits 2 and 3 of the
+// row index swapped) so that the accumulator registers a lane holds are, per
+// 16-key MFMA step, the 8 consecutive keys the P V MFMA expects; v^T is then used
+// in its natural key order.
+//
+// Softmax reference: QK-norm (LayerNorm over the head dim, no affine) gives every
+// normalised q and k a norm of at most sqrt(256) = 16, so every logit
+// q.k / 16 lies in [-16, 16]. The kernel subtracts a fixed reference of 16.25
+// (a margin for bf16 rounding of q and k) instead of a running maximum: softmax
+// is invariant to the shift, p stays in [e^-33, 1] (no overflow, no denormals),
+// and the running-max bookkeeping and the rescaling of O disappear.
+//
+// K and v^T tiles move global -> LDS with gfx950 direct loads
+// (global_load_lds_dwordx4), two stages (2 x 64 KB); 16-byte chunks are XOR
+// swizzled by row so both operand reads are bank-conflict free.
 #include "af_internal.h"
 
 namespace af {
@@ -27,10 +37,16 @@ namespace {
 constexpr int HD = 256;
 constexpr int QT = 128;  // queries per workgroup
 constexpr int KT = 64;   // keys per tile
+constexpr int KTILE = KT * HD;   // bf16 elements of a K (or v^T) tile
+constexpr float REF_LOGIT = 16.25f;
 
-// K tile: [64 keys][256] bf16, 32 chunks of 16 B per row, chunk ^= row & 15.
-__device__ __forceinline__ int kswz(int row) { return row & 15; }
-// V^T tile: [256 hd][64 keys] bf16, 8 chunks per row, chunk ^= f(row).
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void glb_void;
+
+__device__ __forceinline__ int swap23(int x) { return (x & ~12) | ((x >> 1) & 4) | ((x << 1) & 8); }
+// K tile [64 keys][256]: 32 chunks per row, chunk ^= swap23(row & 15).
+__device__ __forceinline__ int kswz(int row) { return swap23(row & 15); }
+// v^T tile [256 hd][64 keys]: 8 chunks per row, chunk ^= (row & 7) ^ ((row >> 3) & 1).
 __device__ __forceinline__ int vswz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 }  // namespace
 
@@ -38,27 +54,77 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_attention_bf16(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
                       const bf16_t* __restrict__ Vt, const float* __restrict__ bias, RowGeom g, int H,
                       int S_pad, bf16_t* __restrict__ O, int d, float scale_log2) {
-    __shared__ __attribute__((aligned(16))) bf16_t sK[KT * HD];
-    __shared__ __attribute__((aligned(16))) bf16_t sV[HD * KT];
-    __shared__ float sBias[KT];
+    // K0 V0 K1 V1, then per stage and wave a 1 KB bias slot (4 copies of 64 fp32 keys)
+    __shared__ __attribute__((aligned(1024))) bf16_t smem[4 * KTILE + 2 * 4 * 512];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int grp = lane >> 5, l32 = lane & 31;
     const int b = blockIdx.z, h = blockIdx.y;
     const int S = g.S();
     const int q0 = blockIdx.x * QT + wave * 32;
     const long bh = (long)b * H + h;
-    const bf16_t* Qbh = Q + bh * S_pad * HD;
     const bf16_t* Kbh = K + bh * S_pad * HD;
     const bf16_t* Vbh = Vt + bh * HD * (long)S_pad;
     const float* biasb = bias + (long)b * S_pad;
 
+    // Direct-load source offsets. K: instruction j of this wave fills tile rows
+    // 2 cb, 2 cb + 1 (cb = 8 wave + j), lane -> row 2 cb + (lane >> 5), physical
+    // chunk lane & 31. v^T: instruction j fills hd rows 8 cb .. 8 cb + 7, lane ->
+    // row 8 cb + (lane >> 3), physical chunk lane & 7.
+    uint32_t koff[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        int row = 2 * (wave * 8 + j) + grp;
+        int lc = (lane & 31) ^ kswz(row);
+        koff[j] = (uint32_t)(row * HD + lc * 8);
+    }
+    uint32_t voff[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        int row = 8 * (wave * 8 + j) + (lane >> 3);
+        int lc = (lane & 7) ^ vswz(row);
+        voff[j] = (uint32_t)(row * S_pad + lc * 8);
+    }
+    auto issue = [&](int k0, int stage) {
+        bf16_t* sK = smem + stage * 2 * KTILE;
+        bf16_t* sV = sK + KTILE;
+        const bf16_t* ksrc = Kbh + (long)k0 * HD;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            __builtin_amdgcn_global_load_lds((glb_void*)(ksrc + koff[j]), (lds_void*)(sK + (wave * 8 + j) * 512), 16, 0,
+                                             0);
+        const bf16_t* vsrc = Vbh + k0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            __builtin_amdgcn_global_load_lds((glb_void*)(vsrc + (long)(j & ~1) * 8 * S_pad + voff[j & 1]),
+                                             (lds_void*)(sV + (wave * 8 + j) * 512), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((glb_void*)(biasb + k0 + (lane & 15) * 4), (lds_void*)(smem + 4 * KTILE + (stage * 4 + wave) * 512), 16,
+                                         0, 0);
+    };
+
     // The wave's 32 queries as MFMA B operands: lane holds query q0 + (lane & 31),
-    // head dims [16 s + 8 (lane >> 5), +8) for k-step s.
+    // head dims [16 s + 8 (lane >> 5), +8) for k-step s. The workgroup's 128 x 256
+    // query tile is staged through the (still idle) second LDS stage so the
+    // registers come from LDS reads.
     bf16x8 qf[16];
     {
-        const bf16_t* qrow = Qbh + (long)(q0 + (lane & 31)) * HD + (lane >> 5) * 8;
+        bf16_t* sQ = smem + 2 * KTILE;                 // 64 KB: rows of 512 B
+        const bf16_t* qsrc = Q + (bh * S_pad + (long)blockIdx.x * QT) * HD;
+        // 128 rows x 32 chunks = 64 instructions of 1 KB, 16 per wave; lane -> row
+        // 2 cb + (lane >> 5), physical chunk lane & 31, logical chunk pc ^ (row & 31).
 #pragma unroll
-        for (int s = 0; s < 16; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qrow + s * 16);
+        for (int j = 0; j < 16; ++j) {
+            int cb = wave * 16 + j;
+            int row = 2 * cb + grp;
+            int lc = (lane & 31) ^ (row & 31);
+            __builtin_amdgcn_global_load_lds((glb_void*)(qsrc + row * HD + lc * 8), (lds_void*)(sQ + cb * 512), 16, 0, 0);
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        const int row = wave * 32 + l32;
+#pragma unroll
+        for (int s = 0; s < 16; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(sQ + row * HD + (((2 * s + grp) ^ (row & 31)) * 8));
+        __syncthreads();
     }
 
     f32x16 o[8];
@@ -66,114 +132,114 @@ void k_attention_bf16(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K
     for (int t = 0; t < 8; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[t][r] = 0.f;
-    float m_run = -INFINITY, l_run = 0.f;
+    float l_run = 0.f;
+    const float ref = REF_LOGIT * 1.4426950408889634f;
 
     const int ntiles = (S + KT - 1) / KT;
+    issue(0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    // K rows this lane feeds to the S^T MFMA of sub-tile t: t*32 + swap23(lane & 31).
+    const int krow0 = swap23(l32);
     for (int kt = 0; kt < ntiles; ++kt) {
-        const int k0 = kt * KT;
-        // ---- stage K tile and v^T tile in LDS
-#pragma unroll
-        for (int p = 0; p < 8; ++p) {
-            int idx = p * 256 + tid;          // 2048 chunks of 16 B
-            int row = idx >> 5, ch = idx & 31;
-            uint4 v = *reinterpret_cast<const uint4*>(Kbh + (long)(k0 + row) * HD + ch * 8);
-            *reinterpret_cast<uint4*>(sK + row * HD + ((ch ^ kswz(row)) * 8)) = v;
-        }
-#pragma unroll
-        for (int p = 0; p < 8; ++p) {
-            int idx = p * 256 + tid;          // 256 rows x 8 chunks
-            int row = idx >> 3, ch = idx & 7; // chunk ch holds keys 8 ch .. 8 ch + 7
-            uint4 v = *reinterpret_cast<const uint4*>(Vbh + (long)row * S_pad + k0 + ch * 8);
-            // key k = 32 t + 8 i + 4 g + j goes to position (2 t + i/2) * 16 + 8 g + 4 (i%2) + j
-            int t = ch >> 2, i = ch & 3;
-            int base = (2 * t + (i >> 1)) * 16 + 4 * (i & 1);
-            int c0 = (base >> 3), off = base & 7;      // 16-byte chunk index and offset (g = 0)
-            bf16_t* rowp = sV + row * KT;
-            *reinterpret_cast<uint2*>(rowp + ((c0 ^ vswz(row)) * 8) + off) = make_uint2(v.x, v.y);
-            *reinterpret_cast<uint2*>(rowp + (((c0 + 1) ^ vswz(row)) * 8) + off) = make_uint2(v.z, v.w);
-        }
-        if (tid < KT) sBias[tid] = biasb[k0 + tid];
-        __syncthreads();
+        const int stage = kt & 1;
+        const bf16_t* sK = smem + stage * 2 * KTILE;
+        const bf16_t* sV = sK + KTILE;
+        const float* sB = reinterpret_cast<const float*>(smem + 4 * KTILE + (stage * 4 + wave) * 512);
 
-        // ---- S^T = K Q^T for two 32-key sub-tiles
+        // ---- S^T starts at the key bias (0, or -inf for excluded keys); register
+        //      (t, i, j) of a lane holds key t*32 + (i/2)*16 + grp*8 + (i%2)*4 + j.
+        //      Read before the next tile's loads are issued.
         f32x16 st[2];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) st[t][r] = 0.f;
-            const int row = t * 32 + (lane & 31);
-#pragma unroll
-            for (int s = 0; s < 16; ++s) {
-                int ch = (2 * s + (lane >> 5)) ^ kswz(row);
-                bf16x8 a = *reinterpret_cast<const bf16x8*>(sK + row * HD + ch * 8);
-                st[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], st[t], 0, 0, 0);
-            }
-        }
-
-        // ---- online softmax (one query per lane, keys spread over regs and the lane^32 partner)
-        float mx = -INFINITY;
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                int key = t * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-                float v = st[t][r] * scale_log2 + sBias[key];
-                st[t][r] = v;
-                mx = fmaxf(mx, v);
+            for (int i = 0; i < 4; ++i) {
+                const float4 bv = *reinterpret_cast<const float4*>(sB + t * 32 + (i >> 1) * 16 + grp * 8 + (i & 1) * 4);
+                st[t][i * 4 + 0] = bv.x;
+                st[t][i * 4 + 1] = bv.y;
+                st[t][i * 4 + 2] = bv.z;
+                st[t][i * 4 + 3] = bv.w;
             }
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float m_new = fmaxf(m_run, mx);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = exp2f(m_run - m_use);
+        if (kt + 1 < ntiles) issue((kt + 1) * KT, stage ^ 1);
+
+        // ---- S^T += K Q^T: two independent 32-key chains; K fragments read three
+        //      k-steps ahead of their MFMAs.
+        constexpr int KD = 3;
+        bf16x8 kf[KD + 1][2];
+        auto kload = [&](int s, bf16x8* dst) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const int row = t * 32 + krow0;
+                const int ch = (2 * s + grp) ^ kswz(row);
+                dst[t] = *reinterpret_cast<const bf16x8*>(sK + row * HD + ch * 8);
+            }
+        };
+#pragma unroll
+        for (int s = 0; s < KD; ++s) kload(s, kf[s]);
+#pragma unroll
+        for (int s = 0; s < 16; ++s) {
+            if (s + KD < 16) kload(s + KD, kf[(s + KD) % (KD + 1)]);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+                st[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s % (KD + 1)][t], qf[s], st[t], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+
+        // ---- first v^T fragments go out before the exponentials
+        constexpr int VD = 4;
+        bf16x8 vf[VD + 1];
+        auto vload = [&](int idx, bf16x8& dst) {      // idx = s4 * 8 + ht
+            const int s4 = idx >> 3, ht = idx & 7;
+            const int row = ht * 32 + l32;
+            const int ch = (2 * s4 + grp) ^ vswz(row);
+            dst = *reinterpret_cast<const bf16x8*>(sV + row * KT + ch * 8);
+        };
+#pragma unroll
+        for (int x = 0; x < VD; ++x) vload(x, vf[x]);
+
+        // ---- P = exp2(S * log2(e)/16 - ref)
+        bf16x8 pb[4];
         float psum = 0.f;
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float p = exp2f(st[t][r] - m_use);
-                st[t][r] = p;
-                psum += p;
+            for (int i = 0; i < 4; ++i) {
+                float p0 = exp2f(st[t][i * 4 + 0] * scale_log2 - ref);
+                float p1 = exp2f(st[t][i * 4 + 1] * scale_log2 - ref);
+                float p2 = exp2f(st[t][i * 4 + 2] * scale_log2 - ref);
+                float p3 = exp2f(st[t][i * 4 + 3] * scale_log2 - ref);
+                psum += (p0 + p1) + (p2 + p3);
+                const int s4 = t * 2 + (i >> 1);
+                const int half = i & 1;
+                union { bf16x8 v; uint32_t u[4]; } pk;
+                pk.v = pb[s4];
+                pk.u[half * 2 + 0] = pack2bf(p0, p1);
+                pk.u[half * 2 + 1] = pack2bf(p2, p3);
+                pb[s4] = pk.v;
             }
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
-#pragma unroll
-        for (int t = 0; t < 8; ++t)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
+        l_run += psum;
 
-        // ---- P as B operands: k-step s4 takes sub-tile t = s4/2, register groups i0 = 2 (s4%2), i0 + 1
-        bf16x8 pb[4];
+        // ---- O^T += V^T P^T: 8 independent head-dim chains per key step, v^T
+        //      fragments read four MFMAs ahead.
 #pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4) {
-            const int t = s4 >> 1, i0 = 2 * (s4 & 1);
-            union { uint32_t u[4]; bf16x8 v; } pk;
-            pk.u[0] = pack2bf(st[t][i0 * 4 + 0], st[t][i0 * 4 + 1]);
-            pk.u[1] = pack2bf(st[t][i0 * 4 + 2], st[t][i0 * 4 + 3]);
-            pk.u[2] = pack2bf(st[t][i0 * 4 + 4], st[t][i0 * 4 + 5]);
-            pk.u[3] = pack2bf(st[t][i0 * 4 + 6], st[t][i0 * 4 + 7]);
-            pb[s4] = pk.v;
+        for (int x = 0; x < 32; ++x) {
+            if (x + VD < 32) vload(x + VD, vf[(x + VD) % (VD + 1)]);
+            __builtin_amdgcn_sched_barrier(0);
+            o[x & 7] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[x % (VD + 1)], pb[x >> 3], o[x & 7], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
         }
-
-        // ---- O^T += V^T P^T
-#pragma unroll
-        for (int ht = 0; ht < 8; ++ht) {
-            const int row = ht * 32 + (lane & 31);
-#pragma unroll
-            for (int s4 = 0; s4 < 4; ++s4) {
-                int ch = (2 * s4 + (lane >> 5)) ^ vswz(row);
-                bf16x8 a = *reinterpret_cast<const bf16x8*>(sV + row * KT + ch * 8);
-                o[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[s4], o[ht], 0, 0, 0);
-            }
-        }
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
 
     // ---- normalise and store: lane has query q0 + (lane & 31), head dims ht*32 + i*8 + 4 (lane>>5) + j
     const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
     const float inv = 1.f / l_tot;
-    const int q = q0 + (lane & 31);
+    const int q = q0 + l32;
     if (q < S) {
-        bf16_t* orow = O + (long)g.row_of(b, q) * d + h * HD + (lane >> 5) * 4;
+        bf16_t* orow = O + (long)g.row_of(b, q) * d + h * HD + grp * 4;
 #pragma unroll
         for (int ht = 0; ht < 8; ++ht)
 #pragma unroll
@@ -185,8 +251,8 @@ void k_attention_bf16(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K
     }
 }
 
-hipError_t attention_bf16(const bf16_t* q, const bf16_t* k, const bf16_t* vt, const float* bias, RowGeom g,
-                          int H, int S_pad, bf16_t* o, int d, hipStream_t s) {
+hipError_t attention_bf16(const bf16_t* q, const bf16_t* k, const bf16_t* vt, const float* bias, RowGeom g, int H,
+                          int S_pad, bf16_t* o, int d, hipStream_t s) {
     int S = g.S();
     if (g.B == 0 || S == 0) return hipSuccess;
     const float scale_log2 = 1.4426950408889634f / 16.0f;  // log2(e) / sqrt(256)
