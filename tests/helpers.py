@@ -58,3 +58,31 @@ def to_dev(x, dtype=None):
     if dtype is not None:
         t = t.to(dtype)
     return t.cuda()
+
+
+class PrefetchWeights:
+    """Oracle weight getter that draws one block's tensors at a time with a thread
+    pool (same seeded streams as oracle.Weights.seeded) and keeps only that block.
+    Test-side plumbing so a full-size oracle forward streams 27 GB of weights."""
+
+    def __init__(self, cfg, seed=0, bf16=True, threads=16):
+        from concurrent.futures import ThreadPoolExecutor
+        self.cfg = cfg
+        self._base = oracle.Weights.seeded(cfg, seed=seed, bf16=bf16)
+        self._specs = oracle.weight_specs(cfg)
+        self._cache = {}
+        self._pool = ThreadPoolExecutor(threads)
+
+    @staticmethod
+    def _group(name):
+        return name.rsplit(".", 1)[0] if "." in name else "_embed"
+
+    def __getitem__(self, name):
+        if name not in self._cache:
+            grp = self._group(name)
+            names = [n for n, _, _ in self._specs if self._group(n) == grp]
+            self._cache = dict(zip(names, self._pool.map(lambda n: self._base[n], names)))
+        return self._cache[name]
+
+    def as_weights(self):
+        return oracle.Weights(self.cfg, self.__getitem__)

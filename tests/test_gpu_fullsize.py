@@ -1,0 +1,134 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the bench
+times: the full AuraFlow transformer (4 joint + 32 single blocks, d = 3072,
+12 x 256 heads, FFN 8192, 96 x 96 PE table) at 1024^2 and 1536^2 with CFG
+batch 2, and the 25-step sampling loop with 4 images (transformer batch 8).
+
+Oracle comparisons use the float32 oracle with the same bf16-rounded weights and
+text; the bar is max|d|/max|ref| <= 2e-2 and cosine >= 0.999 per block output.
+Where the oracle cannot follow (25 steps at batch 8), properties that hold at
+any size are checked bit for bit.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import seeded_inputs
+from helpers import PrefetchWeights, cosine, oracle_cfg, rel_max, to_dev, workload_inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL, COS = 2e-2, 0.999
+
+
+@pytest.fixture(scope="module")
+def full(af):
+    import torch
+    assert torch.cuda.is_available()
+    cfg = af.make_config(max_batch=8, max_latent_h=192, max_latent_w=192, max_text_len=256)
+    m = af.AuraFlowModel(cfg)
+    m.load_seeded_weights(seed=0, threads=16)
+    yield cfg, m
+    m.close()
+
+
+def _inputs(H, W):
+    lengths = seeded_inputs.valid_lengths(2, 16, 256)
+    lat, taus, text, mask = workload_inputs(2, 4, H, W, 256, 2048, lengths=lengths, cfg_pairs=True)
+    return lat, taus, oracle.round_bf16(text), mask
+
+
+@pytest.mark.timeout(1200)
+def test_full_1024_every_sampled_block_and_output(af, full):
+    import torch
+    cfg, m = full
+    ocfg = oracle_cfg(cfg)
+    lat, taus, text, mask = _inputs(128, 128)
+    dev = (to_dev(lat), to_dev(taus), to_dev(text), to_dev(mask))
+    blocks = (0, 3, 4, 12, 24, 35)
+    got = {b: m.forward_taps(*dev, stop_after_block=b).cpu().numpy() for b in blocks}
+    out = m.forward(*dev).cpu().numpy()
+    torch.cuda.synchronize()
+    taps = {}
+    W = PrefetchWeights(ocfg).as_weights()
+    ref = oracle.forward(ocfg, W, lat, taus, text, mask, np.float32,
+                         taps=lambda i, xt, xi: taps.__setitem__(i, np.concatenate([xt, xi], 1)) if i in blocks else None)
+    for b in blocks:
+        e, c = rel_max(got[b], taps[b]), cosine(got[b], taps[b])
+        print(f"block {b}: rel {e:.3e} cos {c:.6f}")
+        assert e <= TOL and c >= COS, (b, e, c)
+    e, c = rel_max(out, ref), cosine(out, ref)
+    print(f"output: rel {e:.3e} cos {c:.6f}")
+    assert e <= TOL and c >= COS, (e, c)
+
+
+def test_full_1024_deterministic_and_mask_invariant(af, full):
+    import torch
+    cfg, m = full
+    lat, taus, text, mask = _inputs(128, 128)
+    dev = (to_dev(lat), to_dev(taus), to_dev(text), to_dev(mask))
+    a = m.forward(*dev).cpu().numpy()
+    b = m.forward(*dev).cpu().numpy()
+    assert np.isfinite(a).all()
+    np.testing.assert_array_equal(a, b)
+    text2 = text.copy()
+    text2[mask == 0] = -3.0
+    c = m.forward(dev[0], dev[1], to_dev(text2), dev[3]).cpu().numpy()
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(a, c)
+
+
+@pytest.mark.timeout(900)
+def test_full_1536_first_joint_block(af, full):
+    import torch
+    cfg, m = full
+    ocfg = oracle_cfg(cfg)
+    lat, taus, text, mask = _inputs(192, 192)       # 96 x 96 patches: the whole PE grid
+    dev = (to_dev(lat), to_dev(taus), to_dev(text), to_dev(mask))
+    got0 = m.forward_taps(*dev, stop_after_block=0).cpu().numpy()
+    out = m.forward(*dev).cpu().numpy()
+    torch.cuda.synchronize()
+    assert np.isfinite(out).all() and out.shape == (2, 4, 192, 192)
+    W = PrefetchWeights(ocfg).as_weights()
+    temb, xt, xi, kv = oracle.embed(ocfg, W, lat, taus, text, mask, np.float32)
+    blk = lambda p: {k: W[p + k] for k in ("ada", "wq", "wk", "wv", "wo", "ff1", "ff2", "ff3")}
+    xt, xi = oracle.joint_block(ocfg, blk("joint0.img."), blk("joint0.txt."), temb, xt, xi, kv, np.float32)
+    ref0 = np.concatenate([xt, xi], 1)
+    e, c = rel_max(got0, ref0), cosine(got0, ref0)
+    print(f"1536 block 0: rel {e:.3e} cos {c:.6f}")
+    assert e <= TOL and c >= COS, (e, c)
+
+
+def test_full_sampling_loop_batch_composition(af, full):
+    """25-step CFG sampling of 4 images (transformer batch 8): every image's
+    trajectory is bit-identical to sampling it alone, and the loop equals the
+    explicit forward + Euler-CFG composition."""
+    import torch
+    cfg, m = full
+    Bp, T = 4, 256
+    x0 = seeded_inputs.latents(Bp, 4, 128, 128)
+    text_u = seeded_inputs.text_embeddings(Bp, T, 2048, first_index=100)
+    text_c = seeded_inputs.text_embeddings(Bp, T, 2048, first_index=200)
+    len_u = seeded_inputs.valid_lengths(Bp, 16, T, seed=5)
+    len_c = seeded_inputs.valid_lengths(Bp, 16, T, seed=6)
+    text = np.concatenate([text_u, text_c])
+    mask = seeded_inputs.length_mask(np.concatenate([len_u, len_c]), T)
+    x = to_dev(x0)
+    m.sample(x, to_dev(text), to_dev(mask), num_steps=25, shift=1.73, guidance=3.5)
+    xb = x.cpu().numpy()
+    assert np.isfinite(xb).all()
+    i = 2
+    xi = to_dev(x0[i:i + 1])
+    ti = np.concatenate([text_u[i:i + 1], text_c[i:i + 1]])
+    mi = np.concatenate([mask[i:i + 1], mask[Bp + i:Bp + i + 1]])
+    m.sample(xi, to_dev(ti), to_dev(mi), num_steps=25, shift=1.73, guidance=3.5)
+    np.testing.assert_array_equal(xi.cpu().numpy()[0], xb[i])
+    # The loop's step is the explicit forward + Euler-CFG composition (one step).
+    sig1 = af.af_sigma_schedule(1, 1.73)
+    xin = to_dev(np.concatenate([x0, x0]))
+    xs1 = to_dev(x0)
+    v1 = m.forward(xin, to_dev(np.full(2 * Bp, sig1[0], np.float32)), to_dev(text), to_dev(mask))
+    af.af_flow_euler_cfg_step(xs1, v1, float(sig1[0]), float(sig1[1]), 3.5)
+    x1 = to_dev(x0)
+    m.sample(x1, to_dev(text), to_dev(mask), num_steps=1, shift=1.73, guidance=3.5)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(x1.cpu().numpy(), xs1.cpu().numpy())
