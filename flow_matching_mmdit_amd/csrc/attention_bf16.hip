@@ -199,37 +199,45 @@ void k_attention_bf16(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K
 #pragma unroll
         for (int x = 0; x < VD; ++x) vload(x, vf[x]);
 
-        // ---- P = exp2(S * log2(e)/16 - ref)
-        bf16x8 pb[4];
+        // ---- P = exp2(S * log2(e)/16 - ref) for key step s4 (16 keys): the lane's
+        //      8 values are registers (t, i, j), t = s4/2, i in {2 (s4%2), +1}.
         float psum = 0.f;
+        auto p_elem = [&](int s4, int e) {
+            const int t = s4 >> 1, i = 2 * (s4 & 1) + (e >> 2), j = e & 3;
+            return __builtin_amdgcn_exp2f(st[t][i * 4 + j] * scale_log2 - ref);   // v_exp_f32; argument >= -48 or -inf
+        };
+        auto pack8 = [&](const float* pf) {
+            union { bf16x8 v; uint32_t u[4]; } pk;
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+            for (int q2 = 0; q2 < 4; ++q2) pk.u[q2] = pack2bf(pf[2 * q2], pf[2 * q2 + 1]);
+            return pk.v;
+        };
+        bf16x8 pb[4];
+        {
+            float pf[8];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float p0 = exp2f(st[t][i * 4 + 0] * scale_log2 - ref);
-                float p1 = exp2f(st[t][i * 4 + 1] * scale_log2 - ref);
-                float p2 = exp2f(st[t][i * 4 + 2] * scale_log2 - ref);
-                float p3 = exp2f(st[t][i * 4 + 3] * scale_log2 - ref);
-                psum += (p0 + p1) + (p2 + p3);
-                const int s4 = t * 2 + (i >> 1);
-                const int half = i & 1;
-                union { bf16x8 v; uint32_t u[4]; } pk;
-                pk.v = pb[s4];
-                pk.u[half * 2 + 0] = pack2bf(p0, p1);
-                pk.u[half * 2 + 1] = pack2bf(p2, p3);
-                pb[s4] = pk.v;
-            }
-        l_run += psum;
+            for (int e = 0; e < 8; ++e) pf[e] = p_elem(0, e), psum += pf[e];
+            pb[0] = pack8(pf);
+        }
 
         // ---- O^T += V^T P^T: 8 independent head-dim chains per key step, v^T
-        //      fragments read four MFMAs ahead.
+        //      fragments read four MFMAs ahead; the exponentials of key step
+        //      s4 + 1 are computed one per MFMA of step s4.
+        float pn[8];
 #pragma unroll
         for (int x = 0; x < 32; ++x) {
+            const int s4 = x >> 3, sub = x & 7;
             if (x + VD < 32) vload(x + VD, vf[(x + VD) % (VD + 1)]);
             __builtin_amdgcn_sched_barrier(0);
-            o[x & 7] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[x % (VD + 1)], pb[x >> 3], o[x & 7], 0, 0, 0);
+            o[x & 7] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[x % (VD + 1)], pb[s4], o[x & 7], 0, 0, 0);
+            if (s4 + 1 < 4) {
+                pn[sub] = p_elem(s4 + 1, sub);
+                psum += pn[sub];
+                if (sub == 7) pb[s4 + 1] = pack8(pn);
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
+        l_run += psum;
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }

@@ -42,7 +42,7 @@ constexpr int RPI = 1024 / (BK * 2);   // tile rows per 1 KB direct-load instruc
 constexpr int TILE_ELEMS = BM * BK;    // bf16 elements of one staged A (or W) tile
 static_assert(2 * STAGES * TILE_ELEMS <= 4 * 64 * 256, "operand stages exceed 128 KB");
 constexpr int NXCD = 8;              // MI355X: 8 XCDs, blocks dispatched round-robin
-constexpr int GROUP_M = 4;
+constexpr int GROUP_M = 8;
 #ifndef GEMM_WM
 #define GEMM_WM 4   // waves along M
 #endif
@@ -166,11 +166,13 @@ void k_gemm_bf16(GemmLaunch L) {
             b[nt] = *reinterpret_cast<const bf16x8*>(sB + r * BK + c * 8);
         }
     };
-    auto compute = [&](const bf16_t* sA, const bf16_t* sB) {
+    // `side(ks)` runs at the top of each k-step (used to spread the next tile's loads).
+    auto compute = [&](const bf16_t* sA, const bf16_t* sB, auto&& side) {
         bf16x8 a[2][MT], b[2][NT];
         load_frags(sA, sB, 0, a[0], b[0]);
 #pragma unroll
         for (int ks = 0; ks < BK / 16; ++ks) {
+            side(ks);
             if (ks + 1 < BK / 16) load_frags(sA, sB, ks + 1, a[(ks + 1) & 1], b[(ks + 1) & 1]);
             __builtin_amdgcn_sched_barrier(0);   // keep the reads of step ks + 1 ahead of these MFMAs
 #pragma unroll
@@ -207,9 +209,28 @@ void k_gemm_bf16(GemmLaunch L) {
         if (t < KT) issue(t);
     wait_landed(min(STAGES - 2, KT - 1));
     for (int kt = 0; kt < KT; ++kt) {
-        if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1);
+        // The next tile's direct loads are spread over the k-steps of this tile's
+        // MFMAs rather than issued in one burst.
+        const int tnext = kt + STAGES - 1;
+        const bool more = tnext < KT;
         const bf16_t* cur = stage_ptr(kt % STAGES);
-        compute(cur, cur + TILE_ELEMS);
+        bf16_t* dst = stage_ptr(tnext % STAGES);
+        constexpr int PER = (BM / RPI) / NW;
+        constexpr int KS = BK / 16;
+        static_assert(PER % KS == 0, "loads per k-step");
+        compute(cur, cur + TILE_ELEMS, [&](int ks) {
+            if (!more) return;
+#pragma unroll
+            for (int jj = 0; jj < PER / KS; ++jj) {
+                const int j = ks * (PER / KS) + jj;
+                __builtin_amdgcn_global_load_lds(
+                    (glb_void*)(Atile + tnext * BK + (long)(j & ~1) * RPI * lda + aoff[j & 1]),
+                    (lds_void*)(dst + (wave * PER + j) * 512), 16, 0, 0);
+                __builtin_amdgcn_global_load_lds(
+                    (glb_void*)(Wtile + tnext * BK + (long)(j & ~1) * RPI * ldw + woff[j & 1]),
+                    (lds_void*)(dst + TILE_ELEMS + (wave * PER + j) * 512), 16, 0, 0);
+            }
+        });
         // tiles issued after kt + 1: kt + 2 .. min(kt + STAGES - 1, KT - 1)
         wait_landed(max(0, min(kt + STAGES - 1, KT - 1) - (kt + 1)));
     }
