@@ -11,18 +11,22 @@
 //   SWIGLU         silu(gate) * up of the interleaved FFN columns
 //                  ([PIPE] 深入源码, 前馈网络)
 //
-// Tiling: 256 x 256 block tile, BK = 64, eight waves (two per SIMD) in a 4 x 2
+// Tiling: 256 x 256 block tile, eight waves (two per SIMD) in a 4 x 2
 // arrangement, each wave owning a 64 x 128 sub-tile (2 x 4 MFMA tiles, 128 fp32
-// accumulators per lane). A and W tiles move global -> LDS with the gfx950
-// direct loads (global_load_lds_dwordx4: lane i writes LDS bytes [16 i, 16 i + 16)
-// of the instruction's 1 KB block), two stages; the XOR swizzle of 16-byte chunks
-// is applied by choosing which global chunk each lane fetches, so the MFMA
-// operand reads (ds_read_b128) are bank-conflict free. Operand fragments are
-// register double-buffered so LDS reads of k-step ks + 1 overlap the MFMAs of ks.
+// accumulators per lane). K is consumed in sub-tiles of 32 (two MFMA k-steps)
+// that stream global -> LDS through four slots with buffer_load ... lds (lane i
+// writes LDS bytes [16 i, 16 i + 16) of the instruction's 1 KB block; the MUBUF
+// form keeps the compiler's LDS-read waits partial, where the FLAT form of the
+// same direct load makes every LDS wait a full drain). The XOR swizzle of
+// 16-byte chunks is applied by choosing which global chunk each lane fetches, so
+// the MFMA operand reads (ds_read_b128) are bank-conflict free. The loop is
+// rotated so that no k-step starts on an empty register file: the barrier that
+// publishes sub-tile j + 1 sits between the two k-steps of sub-tile j, and the
+// second k-step's MFMAs run while the first fragments of sub-tile j + 1 load.
 // Blocks are mapped to tiles XCD by XCD (consecutive block ids go to different
-// XCDs) and, inside an XCD, in groups of four tile rows so co-resident blocks
-// share A and W panels in that XCD's L2. Up to two row groups with different
-// weights share one launch (the joint blocks' text and image streams).
+// XCDs) and, inside an XCD, in groups of row tiles so co-resident blocks share
+// A and W panels in that XCD's L2. Up to two row groups with different weights
+// share one launch (the joint blocks' text and image streams).
 // Epilogues that write bf16 stage the tile in LDS and store 16-byte chunks.
 #include "af_internal.h"
 
@@ -30,17 +34,11 @@ namespace af {
 
 namespace {
 constexpr int BM = 256, BN = 256;
-#ifndef GEMM_BK
-#define GEMM_BK 64      // k depth of one staged tile (64 or 32)
-#endif
-#ifndef GEMM_STAGES
-#define GEMM_STAGES 2   // LDS stages (prefetch distance STAGES - 1 tiles)
-#endif
-constexpr int BK = GEMM_BK, STAGES = GEMM_STAGES;
+constexpr int BK = 32;                 // k depth of one LDS sub-tile (two MFMA k-steps)
+constexpr int NS = 4;                  // LDS slots (sub-tiles in flight: NS - 1)
 constexpr int CH = BK / 8;             // 16-byte chunks per tile row
 constexpr int RPI = 1024 / (BK * 2);   // tile rows per 1 KB direct-load instruction
-constexpr int TILE_ELEMS = BM * BK;    // bf16 elements of one staged A (or W) tile
-static_assert(2 * STAGES * TILE_ELEMS <= 4 * 64 * 256, "operand stages exceed 128 KB");
+constexpr int TILE_ELEMS = BM * BK;    // bf16 elements of one staged A (or W) sub-tile
 constexpr int NXCD = 8;              // MI355X: 8 XCDs, blocks dispatched round-robin
 constexpr int GROUP_M = 8;
 #ifndef GEMM_WM
@@ -51,37 +49,34 @@ constexpr int GROUP_M = 8;
 #endif
 constexpr int QS = 264;              // QKV epilogue staging row stride (elements)
 constexpr int HS = 136;              // SwiGLU epilogue staging row stride (elements)
-constexpr int SMEM_ELEMS = 256 * QS + 2048;   // >= 4 tiles; + [2][256] x 2 fp32 row statistics
+constexpr int SMEM_ELEMS = 256 * QS + 2048;   // epilogue staging + [2][256] x 2 fp32 row statistics
+static_assert(SMEM_ELEMS >= 2 * NS * TILE_ELEMS, "operand slots exceed the LDS block");
 
 typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) void glb_void;
 
-// Chunk swizzle per row so the 32 rows one MFMA operand read touches spread over
-// all banks (both for 8- and 16-lane LDS issue groups).
-__device__ __forceinline__ int swz(int row) {
-    if constexpr (BK == 64) return (row & 7) ^ ((row >> 3) & 1);
-    else return ((row >> 1) ^ (row >> 3)) & 3;
-}
+// Chunk swizzle per row (4 chunks of 16 B per 64-byte row) so the 32 rows one
+// MFMA operand read touches spread over all banks.
+__device__ __forceinline__ int swz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
 // s_waitcnt immediate that waits until at most n vector-memory operations are
 // outstanding (expcnt and lgkmcnt left unconstrained).
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 __host__ __device__ __forceinline__ int tiles_m(int M) { return (M + BM - 1) / BM; }
 
-// Issues this wave's share of one 256 x BK tile starting at `tile` (uniform): the
-// tile is 256 / RPI blocks of 1 KB (RPI rows each); with NW waves, wave w issues
-// blocks cb = w * PER + j. Lane l fills physical chunk l % CH of row
-// RPI cb + l / CH with logical chunk (l % CH) ^ swz(row). swz depends on cb only
-// through its parity, so two per-lane offsets (off[j & 1]) plus a uniform row
-// step cover all of the wave's instructions.
+// Issues this wave's share of one 256 x BK operand sub-tile: the sub-tile is
+// 256 / RPI blocks of 1 KB (RPI rows each); with NW waves, wave w issues blocks
+// cb = w * PER + j. Lane l fills physical chunk l % CH of row RPI cb + l / CH
+// with logical chunk (l % CH) ^ swz(row). swz depends on cb only through its
+// parity, so two per-lane byte offsets (voff[j & 1]) plus a uniform row step
+// (in the scalar offset, with the sub-tile's k offset `sbase`) cover all of the
+// wave's instructions.
 template <int NW>
-__device__ __forceinline__ void issue_tile(const bf16_t* tile, const uint32_t* off, long ld, bf16_t* lds_tile,
-                                           int wave) {
+__device__ __forceinline__ void issue_tile(__amdgpu_buffer_rsrc_t rsrc, const uint32_t* voff, int sbase, int ldbytes,
+                                           bf16_t* lds_tile, int wave) {
     constexpr int PER = (BM / RPI) / NW;
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
-        const bf16_t* src = tile + (long)(j & ~1) * RPI * ld + off[j & 1];
-        __builtin_amdgcn_global_load_lds((glb_void*)src, (lds_void*)(lds_tile + (wave * PER + j) * 512), 16, 0, 0);
-    }
+    for (int j = 0; j < PER; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(lds_tile + (wave * PER + j) * 512), 16, voff[j & 1],
+                                                 sbase + (j & ~1) * RPI * ldbytes, 0, 0);
 }
 }  // namespace
 
@@ -91,7 +86,6 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(WM
 void k_gemm_bf16(GemmLaunch L) {
     constexpr int NW = WM * WN, NTHR = NW * 64;
     constexpr int TM = BM / WM, TN = BN / WN, MT = TM / 32, NT = TN / 32;
-    static_assert(SMEM_ELEMS >= 2 * STAGES * TILE_ELEMS, "LDS");
     static_assert(((BM / RPI) / NW) % 2 == 0, "per-wave load count must be even");
     __shared__ __attribute__((aligned(1024))) bf16_t smem[SMEM_ELEMS];
 
@@ -128,7 +122,7 @@ void k_gemm_bf16(GemmLaunch L) {
     const int m0 = tm * BM, n0 = tn * BN;
     const int K = L.K;
 
-    // Per-lane element offsets for the direct loads (logical chunk folded in). Rows
+    // Per-lane byte offsets for the direct loads (logical chunk folded in). Rows
     // past M read the padding rows every activation buffer carries (at least one
     // tile of rows past its last real row); their results are never stored.
     uint32_t aoff[2], woff[2];
@@ -136,8 +130,8 @@ void k_gemm_bf16(GemmLaunch L) {
     for (int j = 0; j < 2; ++j) {
         const int r = (wave * ((BM / RPI) / NW) + j) * RPI + lane / CH;
         const int c = (lane % CH) ^ swz(r);
-        aoff[j] = (uint32_t)(r * lda + c * 8);
-        woff[j] = (uint32_t)(r * ldw + c * 8);
+        aoff[j] = (uint32_t)((r * lda + c * 8) * 2);
+        woff[j] = (uint32_t)((r * ldw + c * 8) * 2);
     }
     const bf16_t* Atile = A + (long)m0 * lda;
     const bf16_t* Wtile = W + (long)n0 * ldw;
@@ -150,8 +144,6 @@ void k_gemm_bf16(GemmLaunch L) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    // MFMA operands for k-step ks come from LDS one step ahead (register double
-    // buffer), so the reads of step ks + 1 overlap the MFMAs of step ks.
     auto load_frags = [&](const bf16_t* sA, const bf16_t* sB, int ks, bf16x8* a, bf16x8* b) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
@@ -166,73 +158,77 @@ void k_gemm_bf16(GemmLaunch L) {
             b[nt] = *reinterpret_cast<const bf16x8*>(sB + r * BK + c * 8);
         }
     };
-    // `side(ks)` runs at the top of each k-step (used to spread the next tile's loads).
-    auto compute = [&](const bf16_t* sA, const bf16_t* sB, auto&& side) {
-        bf16x8 a[2][MT], b[2][NT];
-        load_frags(sA, sB, 0, a[0], b[0]);
+    auto mfmas = [&](const bf16x8* a, const bf16x8* b) {
 #pragma unroll
-        for (int ks = 0; ks < BK / 16; ++ks) {
-            side(ks);
-            if (ks + 1 < BK / 16) load_frags(sA, sB, ks + 1, a[(ks + 1) & 1], b[(ks + 1) & 1]);
-            __builtin_amdgcn_sched_barrier(0);   // keep the reads of step ks + 1 ahead of these MFMAs
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt)
-                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks & 1][mt], b[ks & 1][nt], acc[mt][nt],
-                                                                          0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
-        }
+            for (int nt = 0; nt < NT; ++nt)
+                acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mt], b[nt], acc[mt][nt], 0, 0, 0);
+    };
+    // Issue order inside a k-step: the fragment reads for the next k-step, then
+    // the MFMAs with the k-step's direct loads slotted in after the first and the
+    // third MFMA.
+    static_assert(MT * NT == 8 && (BM / RPI) / NW == 2, "issue pattern is laid out for the 4 x 2 wave grid");
+    auto pattern = []() {
+        __builtin_amdgcn_sched_group_barrier(0x100, MT + NT, 0);   // DS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);         // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);         // VMEM (direct load)
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, MT * NT - 3, 0);
     };
 
-    // ---- main loop: STAGES LDS stages. Tile kt + STAGES - 1 streams into the
-    // stage read in iteration kt - 1 while tile kt is multiplied. At the end of an
-    // iteration each wave waits until its loads of tile kt + 1 have landed (the
-    // loads of later tiles may stay in flight) and the barrier publishes them.
-    constexpr int PER2 = 2 * ((BM / RPI) / NW);     // direct loads per wave per tile
+    // ---- main loop. Sub-tile t lives in slot t % NS. In iteration j:
+    //   k-step 0: W half of sub-tile j + NS - 2 -> its slot (held sub-tile j - 2,
+    //             released by barrier j - 1); reads of k-step 1; MFMAs of k-step 0
+    //   wait until this wave's loads of sub-tile j + 1 and all its LDS reads of
+    //   slot j are done; barrier j (publishes sub-tile j + 1, releases slot j - 1)
+    //   k-step 1: A half of sub-tile j + NS - 1 -> slot j - 1; reads of sub-tile
+    //             j + 1's k-step 0; MFMAs of k-step 1.
+    // Loads past the last sub-tile re-read the last one into a free slot, so the
+    // loop body has no branches and the wait counts are the same every iteration.
+    constexpr int PER = (BM / RPI) / NW;     // direct loads per wave per operand per sub-tile
+    constexpr int PER2 = 2 * PER;
     const int KT = K / BK;
-    auto stage_ptr = [&](int st) { return smem + st * 2 * TILE_ELEMS; };
-    auto issue = [&](int t) {
-        bf16_t* dst = stage_ptr(t % STAGES);
-        issue_tile<NW>(Atile + t * BK, aoff, lda, dst, wave);
-        issue_tile<NW>(Wtile + t * BK, woff, ldw, dst + TILE_ELEMS, wave);
+    auto slot_ptr = [&](int st) { return smem + st * 2 * TILE_ELEMS; };
+    const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc((void*)Atile, (short)0, 0x7fffffff, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rW = __builtin_amdgcn_make_buffer_rsrc((void*)Wtile, (short)0, 0x7fffffff, 0x00020000);
+    const int ldab = (int)lda * 2, ldwb = (int)ldw * 2;
+    auto issueA = [&](int t, int st) { issue_tile<NW>(rA, aoff, min(t, KT - 1) * BK * 2, ldab, slot_ptr(st), wave); };
+    auto issueW = [&](int t, int st) {
+        issue_tile<NW>(rW, woff, min(t, KT - 1) * BK * 2, ldwb, slot_ptr(st) + TILE_ELEMS, wave);
     };
-    auto wait_landed = [&](int later) {   // `later` = tiles issued after the one needed
-        if (later >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * PER2));
-        else if (later == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER2));
-        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+#pragma unroll
+    for (int t = 0; t < NS - 2; ++t) {
+        issueA(t, t);
+        issueW(t, t);
+    }
+    issueA(NS - 2, NS - 2);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER2 * (NS - 3) + PER));   // sub-tile 0 landed
+    __builtin_amdgcn_s_barrier();
+    bf16x8 fa0[MT], fb0[NT], fa1[MT], fb1[NT];
+    load_frags(slot_ptr(0), slot_ptr(0) + TILE_ELEMS, 0, fa0, fb0);
+    int cs = 0;
+    for (int j = 0; j < KT; ++j) {
+        const bf16_t* cur = slot_ptr(cs);
+        const int ns = cs + 1 == NS ? 0 : cs + 1;      // slot of j + 1
+        const int fs = cs == 0 ? NS - 1 : cs - 1;      // slot of j - 1
+        const int f2 = fs == 0 ? NS - 1 : fs - 1;      // slot of j - 2
+        issueW(j + NS - 2, f2);
+        load_frags(cur, cur + TILE_ELEMS, 1, fa1, fb1);
+        mfmas(fa0, fb0);
+        pattern();
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER2 * (NS - 3)) & ~(15 << 8));   // and lgkmcnt(0)
         __builtin_amdgcn_s_barrier();
-    };
-    static_assert(STAGES <= 4, "wait_landed covers at most two later tiles");
-#pragma unroll
-    for (int t = 0; t < STAGES - 1; ++t)
-        if (t < KT) issue(t);
-    wait_landed(min(STAGES - 2, KT - 1));
-    for (int kt = 0; kt < KT; ++kt) {
-        // The next tile's direct loads are spread over the k-steps of this tile's
-        // MFMAs rather than issued in one burst.
-        const int tnext = kt + STAGES - 1;
-        const bool more = tnext < KT;
-        const bf16_t* cur = stage_ptr(kt % STAGES);
-        bf16_t* dst = stage_ptr(tnext % STAGES);
-        constexpr int PER = (BM / RPI) / NW;
-        constexpr int KS = BK / 16;
-        static_assert(PER % KS == 0, "loads per k-step");
-        compute(cur, cur + TILE_ELEMS, [&](int ks) {
-            if (!more) return;
-#pragma unroll
-            for (int jj = 0; jj < PER / KS; ++jj) {
-                const int j = ks * (PER / KS) + jj;
-                __builtin_amdgcn_global_load_lds(
-                    (glb_void*)(Atile + tnext * BK + (long)(j & ~1) * RPI * lda + aoff[j & 1]),
-                    (lds_void*)(dst + (wave * PER + j) * 512), 16, 0, 0);
-                __builtin_amdgcn_global_load_lds(
-                    (glb_void*)(Wtile + tnext * BK + (long)(j & ~1) * RPI * ldw + woff[j & 1]),
-                    (lds_void*)(dst + TILE_ELEMS + (wave * PER + j) * 512), 16, 0, 0);
-            }
-        });
-        // tiles issued after kt + 1: kt + 2 .. min(kt + STAGES - 1, KT - 1)
-        wait_landed(max(0, min(kt + STAGES - 1, KT - 1) - (kt + 1)));
+        __builtin_amdgcn_sched_barrier(0);
+        issueA(j + NS - 1, fs);
+        const bf16_t* nxt = slot_ptr(ns);
+        load_frags(nxt, nxt + TILE_ELEMS, 0, fa0, fb0);
+        mfmas(fa1, fb1);
+        pattern();
+        __builtin_amdgcn_sched_barrier(0);
+        cs = ns;
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -266,21 +262,47 @@ void k_gemm_bf16(GemmLaunch L) {
                 for (int nt = 0; nt < NT; ++nt) L.resid[orow * L.N + n0 + lc_base + nt * 32] = acc[mt][nt][r];
             }
     } else if constexpr (EPI == EPI_GATED_RESID) {
+        // Rows in groups of four (one r >> 2 of one mt): the residual and gate loads
+        // of group g + 1 are issued before group g's read-modify-write stores, so a
+        // wave keeps two groups of loads in flight rather than one row's.
+        float* __restrict__ resid = L.resid;
+        const float* __restrict__ mod = L.mod;
+        const int ncol = n0 + lc_base;
+        constexpr int NG = MT * 4;
+        float xv[2][4][NT], gv[2][4][NT];
+        auto grow = [&](int g, int j) { return m0 + lr_base + (g >> 2) * 32 + (g & 3) * 8 + j; };
+        auto load = [&](int g, float (*x)[NT], float (*gt)[NT]) {
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+            for (int j = 0; j < 4; ++j) {
+                const int m = grow(g, j);
+                if (m < M) {
+                    const int rr = row0 + m;
+                    const float* gate = mod + (long)L.geom.batch_of(rr) * L.mod_stride + gate_off + ncol;
+                    const float* xrow = resid + (long)rr * L.N + ncol;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                int m = m0 + lr_base + mt * 32 + (r >> 2) * 8 + (r & 3);
-                if (m >= M) continue;
-                int rr = row0 + m;
-                const float* gate = L.mod + (long)L.geom.batch_of(rr) * L.mod_stride + gate_off;
-                float* xrow = L.resid + (long)rr * L.N;
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) {
-                    int n = n0 + lc_base + nt * 32;
-                    xrow[n] += gate[n] * acc[mt][nt][r];
+                    for (int nt = 0; nt < NT; ++nt) {
+                        x[j][nt] = xrow[nt * 32];
+                        gt[j][nt] = gate[nt * 32];
+                    }
                 }
             }
+        };
+        load(0, xv[0], gv[0]);
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            if (g + 1 < NG) load(g + 1, xv[(g + 1) & 1], gv[(g + 1) & 1]);
+            const int mt = g >> 2, i = g & 3;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int m = grow(g, j);
+                if (m < M) {
+                    float* xrow = resid + (long)(row0 + m) * L.N + ncol;
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt)
+                        xrow[nt * 32] = xv[g & 1][j][nt] + gv[g & 1][j][nt] * acc[mt][nt][i * 4 + j];
+                }
+            }
+        }
     } else if constexpr (EPI == EPI_SWIGLU) {
         // h tile [256 rows][128 cols] bf16 staged in LDS, then 16-byte row stores.
         bf16_t* st = smem;
