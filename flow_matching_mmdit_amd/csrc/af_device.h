@@ -11,36 +11,44 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf2f(bf16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
 
-// Round to nearest, ties to even (inputs are finite).
-__device__ __forceinline__ bf16_t f2bf(float f) {
-    uint32_t u = __float_as_uint(f);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return (bf16_t)(u >> 16);
-}
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
+// fp32 -> bf16, round to nearest, ties to even: gfx950's v_cvt_pk_bf16_f32 (one
+// instruction for two values; for finite inputs it gives the same bits as adding
+// 0x7FFF plus the kept lsb and truncating).
 __device__ __forceinline__ uint32_t pack2bf(float lo, float hi) {
-    return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+    const f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
+__device__ __forceinline__ bf16_t f2bf(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
 
 __device__ __forceinline__ float silu_f(float x) { return x / (1.0f + __expf(-x)); }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+// Lane reductions through DPP (row-local VALU operand swizzles) rather than
+// LDS-routed permutes.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+// Sum over each 16-lane DPP row; every lane receives its row's sum.
+__device__ __forceinline__ float row16_sum(float v) {
+    v += dpp_f<0xB1>(v);    // quad_perm [1,0,3,2]: lane ^ 1
+    v += dpp_f<0x4E>(v);    // quad_perm [2,3,0,1]: lane ^ 2
+    v += dpp_f<0x141>(v);   // row_half_mirror: the other quad of each 8
+    v += dpp_f<0x140>(v);   // row_mirror: the other 8 of each 16
     return v;
 }
-
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-    return v;
-}
-
 // Sum over the 32 lanes that share bit 5 of the lane id (one half-wave).
 __device__ __forceinline__ float half_wave_sum(float v) {
-#pragma unroll
-    for (int o = 16; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
+    v = row16_sum(v);
+    return v + __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));   // lane ^ 16 within 32
+}
+// Sum over all 64 lanes (uniform result).
+__device__ __forceinline__ float wave_sum(float v) {
+    v = half_wave_sum(v);
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0)) +
+           __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
 }
 
 // Residual-row geometry. The fp32 residual stream is stored stream-major:

@@ -26,9 +26,13 @@
 // is invariant to the shift, p stays in [e^-33, 1] (no overflow, no denormals),
 // and the running-max bookkeeping and the rescaling of O disappear.
 //
-// K and v^T tiles move global -> LDS with gfx950 direct loads
-// (global_load_lds_dwordx4), two stages (2 x 64 KB); 16-byte chunks are XOR
-// swizzled by row so both operand reads are bank-conflict free.
+// K and v^T tiles move global -> LDS with gfx950 direct loads (buffer_load ...
+// lds, 16 bytes per lane; the MUBUF form keeps the compiler's LDS-read waits
+// partial), two stages (2 x 64 KB); 16-byte chunks are XOR swizzled by row so
+// both operand reads are bank-conflict free. The next tile's loads are spread
+// over the MFMAs of the current one (K during S^T, v^T and the bias during
+// P V); the last tile re-loads itself into the idle stage so the loop body has
+// no branches.
 #include "af_internal.h"
 
 namespace af {
@@ -41,7 +45,6 @@ constexpr int KTILE = KT * HD;   // bf16 elements of a K (or v^T) tile
 constexpr float REF_LOGIT = 16.25f;
 
 typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) void glb_void;
 
 __device__ __forceinline__ int swap23(int x) { return (x & ~12) | ((x >> 1) & 4) | ((x << 1) & 8); }
 // K tile [64 keys][256]: 32 chunks per row, chunk ^= swap23(row & 15).
@@ -67,39 +70,40 @@ void k_attention_bf16(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K
     const bf16_t* Vbh = Vt + bh * HD * (long)S_pad;
     const float* biasb = bias + (long)b * S_pad;
 
-    // Direct-load source offsets. K: instruction j of this wave fills tile rows
-    // 2 cb, 2 cb + 1 (cb = 8 wave + j), lane -> row 2 cb + (lane >> 5), physical
-    // chunk lane & 31. v^T: instruction j fills hd rows 8 cb .. 8 cb + 7, lane ->
-    // row 8 cb + (lane >> 3), physical chunk lane & 7.
+    // Direct-load source byte offsets. K: instruction j of this wave fills tile
+    // rows 2 cb, 2 cb + 1 (cb = 8 wave + j), lane -> row 2 cb + (lane >> 5),
+    // physical chunk lane & 31. v^T: instruction j fills hd rows 8 cb .. 8 cb + 7,
+    // lane -> row 8 cb + (lane >> 3), physical chunk lane & 7.
     uint32_t koff[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         int row = 2 * (wave * 8 + j) + grp;
         int lc = (lane & 31) ^ kswz(row);
-        koff[j] = (uint32_t)(row * HD + lc * 8);
+        koff[j] = (uint32_t)(row * HD + lc * 8) * 2;
     }
     uint32_t voff[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         int row = 8 * (wave * 8 + j) + (lane >> 3);
         int lc = (lane & 7) ^ vswz(row);
-        voff[j] = (uint32_t)(row * S_pad + lc * 8);
+        voff[j] = (uint32_t)(row * S_pad + lc * 8) * 2;
     }
-    auto issue = [&](int k0, int stage) {
+    const __amdgpu_buffer_rsrc_t rK = __builtin_amdgcn_make_buffer_rsrc((void*)Kbh, (short)0, S_pad * HD * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rV = __builtin_amdgcn_make_buffer_rsrc((void*)Vbh, (short)0, S_pad * HD * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc((void*)biasb, (short)0, S_pad * 4, 0x00020000);
+    // one direct load: K rows / v^T rows (instruction j of 8) / bias of the tile at key k0 into `stage`
+    auto issue_k = [&](int j, int k0, int stage) {
         bf16_t* sK = smem + stage * 2 * KTILE;
-        bf16_t* sV = sK + KTILE;
-        const bf16_t* ksrc = Kbh + (long)k0 * HD;
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            __builtin_amdgcn_global_load_lds((glb_void*)(ksrc + koff[j]), (lds_void*)(sK + (wave * 8 + j) * 512), 16, 0,
-                                             0);
-        const bf16_t* vsrc = Vbh + k0;
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            __builtin_amdgcn_global_load_lds((glb_void*)(vsrc + (long)(j & ~1) * 8 * S_pad + voff[j & 1]),
-                                             (lds_void*)(sV + (wave * 8 + j) * 512), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((glb_void*)(biasb + k0 + (lane & 15) * 4), (lds_void*)(smem + 4 * KTILE + (stage * 4 + wave) * 512), 16,
-                                         0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rK, (lds_void*)(sK + (wave * 8 + j) * 512), 16, koff[j], k0 * HD * 2, 0, 0);
+    };
+    auto issue_v = [&](int j, int k0, int stage) {
+        bf16_t* sV = smem + stage * 2 * KTILE + KTILE;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rV, (lds_void*)(sV + (wave * 8 + j) * 512), 16, voff[j & 1],
+                                                 k0 * 2 + (j & ~1) * 8 * S_pad * 2, 0, 0);
+    };
+    auto issue_b = [&](int k0, int stage) {   // 64 fp32 keys, replicated 4x across the 1 KB slot
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_void*)(smem + 4 * KTILE + (stage * 4 + wave) * 512), 16,
+                                                 (lane & 15) * 16, k0 * 4, 0, 0);
     };
 
     // The wave's 32 queries as MFMA B operands: lane holds query q0 + (lane & 31),
@@ -110,6 +114,7 @@ void k_attention_bf16(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K
     {
         bf16_t* sQ = smem + 2 * KTILE;                 // 64 KB: rows of 512 B
         const bf16_t* qsrc = Q + (bh * S_pad + (long)blockIdx.x * QT) * HD;
+        const __amdgpu_buffer_rsrc_t rQ = __builtin_amdgcn_make_buffer_rsrc((void*)qsrc, (short)0, QT * HD * 2, 0x00020000);
         // 128 rows x 32 chunks = 64 instructions of 1 KB, 16 per wave; lane -> row
         // 2 cb + (lane >> 5), physical chunk lane & 31, logical chunk pc ^ (row & 31).
 #pragma unroll
@@ -117,7 +122,7 @@ void k_attention_bf16(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K
             int cb = wave * 16 + j;
             int row = 2 * cb + grp;
             int lc = (lane & 31) ^ (row & 31);
-            __builtin_amdgcn_global_load_lds((glb_void*)(qsrc + row * HD + lc * 8), (lds_void*)(sQ + cb * 512), 16, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rQ, (lds_void*)(sQ + cb * 512), 16, (row * HD + lc * 8) * 2, 0, 0, 0);
         }
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
@@ -136,7 +141,11 @@ void k_attention_bf16(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K
     const float ref = REF_LOGIT * 1.4426950408889634f;
 
     const int ntiles = (S + KT - 1) / KT;
-    issue(0, 0);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) issue_k(j, 0, 0);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) issue_v(j, 0, 0);
+    issue_b(0, 0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     // K rows this lane feeds to the S^T MFMA of sub-tile t: t*32 + swap23(lane & 31).
@@ -149,7 +158,7 @@ void k_attention_bf16(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K
 
         // ---- S^T starts at the key bias (0, or -inf for excluded keys); register
         //      (t, i, j) of a lane holds key t*32 + (i/2)*16 + grp*8 + (i%2)*4 + j.
-        //      Read before the next tile's loads are issued.
+        //      Read before the next tile's loads are issued (they target the other stage).
         f32x16 st[2];
 #pragma unroll
         for (int t = 0; t < 2; ++t)
@@ -161,7 +170,7 @@ void k_attention_bf16(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K
                 st[t][i * 4 + 2] = bv.z;
                 st[t][i * 4 + 3] = bv.w;
             }
-        if (kt + 1 < ntiles) issue((kt + 1) * KT, stage ^ 1);
+        const int knext = min(kt + 1, ntiles - 1) * KT;   // key of the tile loaded during this one
 
         // ---- S^T += K Q^T: two independent 32-key chains; K fragments read three
         //      k-steps ahead of their MFMAs.
@@ -180,6 +189,7 @@ void k_attention_bf16(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K
 #pragma unroll
         for (int s = 0; s < 16; ++s) {
             if (s + KD < 16) kload(s + KD, kf[(s + KD) % (KD + 1)]);
+            if ((s & 1) == 0) issue_k(s >> 1, knext, stage ^ 1);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int t = 0; t < 2; ++t)
@@ -228,6 +238,8 @@ void k_attention_bf16(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K
         for (int x = 0; x < 32; ++x) {
             const int s4 = x >> 3, sub = x & 7;
             if (x + VD < 32) vload(x + VD, vf[(x + VD) % (VD + 1)]);
+            if ((x & 3) == 0) issue_v(x >> 2, knext, stage ^ 1);
+            if (x == 2) issue_b(knext, stage ^ 1);
             __builtin_amdgcn_sched_barrier(0);
             o[x & 7] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[x % (VD + 1)], pb[s4], o[x & 7], 0, 0, 0);
             if (s4 + 1 < 4) {

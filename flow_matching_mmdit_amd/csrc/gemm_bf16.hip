@@ -401,42 +401,47 @@ void k_gemm_bf16(GemmLaunch L) {
                 }
             }
         } else {
+            // The tile goes to LDS transposed (head column c -> LDS row c, tile rows
+            // along it), four consecutive rows per 8-byte write.
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    int lr = lr_base + mt * 32 + (r >> 2) * 8 + (r & 3);
+                for (int i = 0; i < 4; ++i) {
+                    const int lr = lr_base + mt * 32 + i * 8;
 #pragma unroll
-                    for (int nt = 0; nt < NT; ++nt) st[lr * QS + lc_base + nt * 32] = f2bf(acc[mt][nt][r]);
+                    for (int nt = 0; nt < NT; ++nt) {
+                        const int c = lc_base + nt * 32;
+                        *reinterpret_cast<uint2*>(st + c * QS + lr) =
+                            make_uint2(pack2bf(acc[mt][nt][i * 4 + 0], acc[mt][nt][i * 4 + 1]),
+                                       pack2bf(acc[mt][nt][i * 4 + 2], acc[mt][nt][i * 4 + 3]));
+                    }
                 }
             __syncthreads();
-            // v^T: for head column c, 8 consecutive tile rows -> 8 consecutive keys (one
+            // v^T: 8 consecutive tile rows of head column c -> 8 consecutive keys (one
             // 16-byte store) when they lie in one sample's segment and start 8-aligned;
-            // otherwise element stores.
+            // otherwise element stores. Consecutive lanes take consecutive row chunks
+            // of one column, so 32 lanes read 512 contiguous LDS bytes and write one
+            // 512-byte run of a v^T row.
             bf16_t* vt = (bf16_t*)L.vt;
 #pragma unroll 2
             for (int it = 0; it < 8192 / NTHR; ++it) {
-                int idx = it * NTHR + tid;             // 256 columns x 32 row-chunks
-                int c = idx & 255, rc = idx >> 8;
-                int lr0 = rc * 8;
-                int m = m0 + lr0;
+                const int idx = it * NTHR + tid;       // 256 columns x 32 row-chunks
+                const int rc = idx & 31, c = idx >> 5;
+                const int lr0 = rc * 8;
+                const int m = m0 + lr0;
                 if (m >= M) continue;
-                int rr = row0 + m;
-                int b = L.geom.batch_of(rr), s0 = L.geom.seq_of(rr);
-                bool fast = (m + 7 < M) && (s0 % 8 == 0) && L.geom.batch_of(rr + 7) == b &&
-                            L.geom.seq_of(rr + 7) == s0 + 7;
+                const int rr = row0 + m;
+                const int b = L.geom.batch_of(rr), s0 = L.geom.seq_of(rr);
+                const bool fast = (m + 7 < M) && (s0 % 8 == 0) && L.geom.batch_of(rr + 7) == b &&
+                                  L.geom.seq_of(rr + 7) == s0 + 7;
                 if (fast) {
-                    uint32_t w[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        w[e] = (uint32_t)st[(lr0 + 2 * e) * QS + c] | ((uint32_t)st[(lr0 + 2 * e + 1) * QS + c] << 16);
-                    bf16_t* base = vt + (((long)b * H + head) * 256 + c) * (long)S_pad;
-                    *reinterpret_cast<uint4*>(base + s0) = make_uint4(w[0], w[1], w[2], w[3]);
+                    const uint4 v = *reinterpret_cast<const uint4*>(st + c * QS + lr0);
+                    *reinterpret_cast<uint4*>(vt + (((long)b * H + head) * 256 + c) * (long)S_pad + s0) = v;
                 } else {
                     for (int e = 0; e < 8 && m + e < M; ++e) {
-                        int re = rr + e;
-                        int be = L.geom.batch_of(re), se = L.geom.seq_of(re);
-                        vt[(((long)be * H + head) * 256 + c) * (long)S_pad + se] = st[(lr0 + e) * QS + c];
+                        const int re = rr + e;
+                        const int be = L.geom.batch_of(re), se = L.geom.seq_of(re);
+                        vt[(((long)be * H + head) * 256 + c) * (long)S_pad + se] = st[c * QS + lr0 + e];
                     }
                 }
             }
