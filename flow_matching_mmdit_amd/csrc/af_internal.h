@@ -38,6 +38,7 @@ struct GemmLaunch {
     void* q; void* k; void* vt;        // QKV outputs
     int H, hd, S_pad;
     float eps;
+    float q_scale;                     // QKV: factor on the normalised q before rounding (1 = none)
 };
 
 hipError_t gemm_bf16(const GemmLaunch& L, hipStream_t s);
@@ -45,7 +46,14 @@ hipError_t gemm_f32(const GemmLaunch& L, hipStream_t s);
 
 // ------------------------------------------------------------------ attention
 // q, k: [B, H, S_pad, hd]; v^T: [B, H, hd, S_pad] (bf16 path) or v: [B, H, S_pad, hd] (fp32 path);
-// bias: [B, S_pad] additive key bias (0 or -inf); o: [M, d] in residual row order.
+// bias: [B, S_pad] additive key bias (KEY_KEEP for a kept key, -inf for an
+// excluded one); o: [M, d] in residual row order.
+// The bf16 kernel works in log2 units with a fixed softmax reference: it takes q
+// pre-multiplied by ATTN_BF16_Q_SCALE = log2(e)/sqrt(256) and the bias with
+// KEY_KEEP = ATTN_BF16_KEY_KEEP = -16.25 log2(e) (QK-norm bounds every logit
+// q.k/16 to [-16, 16]); the fp32 kernel takes plain q and KEY_KEEP = 0.
+constexpr float ATTN_BF16_Q_SCALE = 1.4426950408889634f / 16.0f;
+constexpr float ATTN_BF16_KEY_KEEP = -16.25f * 1.4426950408889634f;
 hipError_t attention_bf16(const bf16_t* q, const bf16_t* k, const bf16_t* vt, const float* bias,
                           RowGeom g, int H, int S_pad, bf16_t* o, int d, hipStream_t s);
 hipError_t attention_f32(const float* q, const float* k, const float* v, const float* bias,
@@ -62,7 +70,7 @@ hipError_t patch_embed(const float* lat, int C, int H, int W, int p, const void*
 hipError_t copy_registers(const void* reg, af_dtype wdt, int R, float* resid, RowGeom g, int d,
                           hipStream_t s);
 hipError_t f32_to_bf16(const float* src, bf16_t* dst, long n, hipStream_t s);
-hipError_t key_bias(const uint8_t* mask, int T, int R, RowGeom g, int S_pad, float* bias,
+hipError_t key_bias(const uint8_t* mask, int T, int R, RowGeom g, int S_pad, float keep, float* bias,
                     hipStream_t s);
 // out[r] = LN(x[r]) * (1 + scale) + shift; rows r < split use offsets (sh_a, sc_a), others (sh_b, sc_b)
 hipError_t ln_modulate(const float* x, int M, int d, RowGeom g, int split, const float* mod,

@@ -377,6 +377,7 @@ GemmLaunch gemm_base(af_model* m, RowGeom g, int N, int K, int epi) {
     L.H = m->D.H;
     L.hd = m->D.hd;
     L.eps = m->cfg.ln_eps;
+    L.q_scale = 1.f;
     return L;
 }
 
@@ -423,6 +424,7 @@ af_status run_block(af_model* m, RowGeom g, int S_pad, const BlockW* wt, const B
         ProfScope ps(m, AF_K_GEMM_QKV, s);
         GemmLaunch L = gemm_base(m, g, 3 * d, d, m->dt == AF_BF16 ? EPI_QKV : EPI_STORE);
         L.q = m->q; L.k = m->k; L.vt = m->v; L.S_pad = S_pad;
+        L.q_scale = ATTN_BF16_Q_SCALE;
         L.C = m->raw; L.ldc = 3 * d;
         add_groups(L, (const char*)m->nrm, d, d * es, 0, 0);
         AF_TRY(gemm(m, L, s));
@@ -489,7 +491,7 @@ af_status run_forward(af_model* m, const Inputs& in, int stop_after, float* resi
     // key-padding bias
     {
     ProfScope ps(m, AF_K_EMBED, s);
-    AF_K(key_bias(in.mask, in.T, D.R, g, S_pad, m->kbias, s));
+    AF_K(key_bias(in.mask, in.T, D.R, g, S_pad, m->dt == AF_BF16 ? ATTN_BF16_KEY_KEEP : 0.f, m->kbias, s));
     }
     // timestep embedding and every block's modulation vectors
     {

@@ -3,36 +3,41 @@
 // [TRANS] 注意力处理器与 QKV 融合: text and image q/k/v are concatenated (text
 // first) and one scaled-dot-product attention runs over the whole sequence, no
 // dropout, not causal; the scale is 1/sqrt(head_dim). Keys of padded text
-// tokens are excluded through an additive bias (0 or -inf) per key.
+// tokens are excluded through an additive bias per key.
 //
 // Layout: q, k [B, H, S_pad, 256]; v^T [B, H, 256, S_pad] (written transposed by
 // the QKV GEMM epilogue so the P V contraction reads keys contiguously);
 // output o [M, d] in residual-row order.
 //
+// Scaled inputs: q arrives multiplied by log2(e)/16 (the QKV epilogue applies
+// it before rounding to bf16) and the key bias holds -16.25 log2(e) for a kept
+// key and -inf for an excluded one, so p = exp2(k.q' + bias) needs no other
+// arithmetic. Softmax reference: QK-norm (LayerNorm over the head dim, no
+// affine) gives every normalised q and k a norm of at most sqrt(256) = 16, so
+// every logit q.k / 16 lies in [-16, 16]; the kernel subtracts the fixed
+// reference 16.25 (a margin for bf16 rounding) instead of a running maximum:
+// softmax is invariant to the shift, p stays in [e^-33, 1] (no overflow, no
+// denormals), and the running-max bookkeeping and the rescaling of O disappear.
+// With a fixed reference, partial sums over key tiles simply add.
+//
 // One workgroup = 4 waves = 128 queries of one (b, h); each wave owns 32 queries
 // and keeps them in registers as MFMA B operands. Per 64-key tile:
-//   S^T = K Q^T  (A = K rows from LDS) -> one query per lane (lane & 31),
-//   P = exp2(S^T * log2(e)/16 - ref + bias),
+//   S^T = K Q'^T + bias  (A = K rows from LDS) -> one query per lane (lane & 31),
+//   P = exp2(S^T),
 //   O^T += V^T P^T (A = v^T from LDS, B = P straight from the S^T registers).
 // The K rows each lane feeds to the S^T MFMA are permuted (bits 2 and 3 of the
 // row index swapped) so that the accumulator registers a lane holds are, per
 // 16-key MFMA step, the 8 consecutive keys the P V MFMA expects; v^T is then used
 // in its natural key order.
 //
-// Softmax reference: QK-norm (LayerNorm over the head dim, no affine) gives every
-// normalised q and k a norm of at most sqrt(256) = 16, so every logit
-// q.k / 16 lies in [-16, 16]. The kernel subtracts a fixed reference of 16.25
-// (a margin for bf16 rounding of q and k) instead of a running maximum: softmax
-// is invariant to the shift, p stays in [e^-33, 1] (no overflow, no denormals),
-// and the running-max bookkeeping and the rescaling of O disappear.
-//
-// K and v^T tiles move global -> LDS with gfx950 direct loads (buffer_load ...
-// lds, 16 bytes per lane; the MUBUF form keeps the compiler's LDS-read waits
-// partial), two stages (2 x 64 KB); 16-byte chunks are XOR swizzled by row so
-// both operand reads are bank-conflict free. The next tile's loads are spread
-// over the MFMAs of the current one (K during S^T, v^T and the bias during
-// P V); the last tile re-loads itself into the idle stage so the loop body has
-// no branches.
+// Software pipeline (one wave per SIMD): iteration t runs the S MFMAs of tile
+// t + 1 with the exponentials of tile t interleaved (one MFMA, two p values),
+// then the P V MFMAs of tile t. K and v^T tiles have two LDS slots each, filled
+// by gfx950 direct loads (buffer_load ... lds, 16 bytes per lane; the MUBUF form
+// keeps the compiler's LDS-read waits partial) that are spread over the MFMAs:
+// in iteration t, K and the bias of tile t + 2 and v^T of tile t + 1. One
+// barrier per iteration publishes them and frees the slots. 16-byte chunks are
+// XOR swizzled by row so both operand reads are bank-conflict free.
 #include "af_internal.h"
 
 namespace af {
@@ -42,7 +47,6 @@ constexpr int HD = 256;
 constexpr int QT = 128;  // queries per workgroup
 constexpr int KT = 64;   // keys per tile
 constexpr int KTILE = KT * HD;   // bf16 elements of a K (or v^T) tile
-constexpr float REF_LOGIT = 16.25f;
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -56,8 +60,9 @@ __device__ __forceinline__ int vswz(int row) { return (row & 7) ^ ((row >> 3) & 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_attention_bf16(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
                       const bf16_t* __restrict__ Vt, const float* __restrict__ bias, RowGeom g, int H,
-                      int S_pad, bf16_t* __restrict__ O, int d, float scale_log2) {
-    // K0 V0 K1 V1, then per stage and wave a 1 KB bias slot (4 copies of 64 fp32 keys)
+                      int S_pad, bf16_t* __restrict__ O, int d) {
+    // K slot 0, K slot 1, v^T slot 0, v^T slot 1, then per slot and wave a 1 KB
+    // bias block (4 copies of 64 fp32 keys)
     __shared__ __attribute__((aligned(1024))) bf16_t smem[4 * KTILE + 2 * 4 * 512];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -69,6 +74,9 @@ void k_attention_bf16(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K
     const bf16_t* Kbh = K + bh * S_pad * HD;
     const bf16_t* Vbh = Vt + bh * HD * (long)S_pad;
     const float* biasb = bias + (long)b * S_pad;
+    auto kslot = [&](int i) { return smem + i * KTILE; };
+    auto vslot = [&](int i) { return smem + (2 + i) * KTILE; };
+    auto bslot = [&](int i) { return reinterpret_cast<const float*>(smem + 4 * KTILE + (i * 4 + wave) * 512); };
 
     // Direct-load source byte offsets. K: instruction j of this wave fills tile
     // rows 2 cb, 2 cb + 1 (cb = 8 wave + j), lane -> row 2 cb + (lane >> 5),
@@ -91,28 +99,32 @@ void k_attention_bf16(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K
     const __amdgpu_buffer_rsrc_t rK = __builtin_amdgcn_make_buffer_rsrc((void*)Kbh, (short)0, S_pad * HD * 2, 0x00020000);
     const __amdgpu_buffer_rsrc_t rV = __builtin_amdgcn_make_buffer_rsrc((void*)Vbh, (short)0, S_pad * HD * 2, 0x00020000);
     const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc((void*)biasb, (short)0, S_pad * 4, 0x00020000);
-    // one direct load: K rows / v^T rows (instruction j of 8) / bias of the tile at key k0 into `stage`
-    auto issue_k = [&](int j, int k0, int stage) {
-        bf16_t* sK = smem + stage * 2 * KTILE;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rK, (lds_void*)(sK + (wave * 8 + j) * 512), 16, koff[j], k0 * HD * 2, 0, 0);
+    const int ntiles = (S + KT - 1) / KT;
+    // one direct load of tile `tile` (clamped to the last tile: the loads issued
+    // past the end re-read it into a slot nobody reads again)
+    auto issue_k = [&](int j, int tile, int slot) {
+        const int k0 = min(tile, ntiles - 1) * KT;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rK, (lds_void*)(kslot(slot) + (wave * 8 + j) * 512), 16, koff[j],
+                                                 k0 * HD * 2, 0, 0);
     };
-    auto issue_v = [&](int j, int k0, int stage) {
-        bf16_t* sV = smem + stage * 2 * KTILE + KTILE;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rV, (lds_void*)(sV + (wave * 8 + j) * 512), 16, voff[j & 1],
+    auto issue_v = [&](int j, int tile, int slot) {
+        const int k0 = min(tile, ntiles - 1) * KT;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rV, (lds_void*)(vslot(slot) + (wave * 8 + j) * 512), 16, voff[j & 1],
                                                  k0 * 2 + (j & ~1) * 8 * S_pad * 2, 0, 0);
     };
-    auto issue_b = [&](int k0, int stage) {   // 64 fp32 keys, replicated 4x across the 1 KB slot
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_void*)(smem + 4 * KTILE + (stage * 4 + wave) * 512), 16,
+    auto issue_b = [&](int tile, int slot) {
+        const int k0 = min(tile, ntiles - 1) * KT;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_void*)(smem + 4 * KTILE + (slot * 4 + wave) * 512), 16,
                                                  (lane & 15) * 16, k0 * 4, 0, 0);
     };
 
     // The wave's 32 queries as MFMA B operands: lane holds query q0 + (lane & 31),
     // head dims [16 s + 8 (lane >> 5), +8) for k-step s. The workgroup's 128 x 256
-    // query tile is staged through the (still idle) second LDS stage so the
-    // registers come from LDS reads.
+    // query tile is staged through the (still idle) v^T slots so the registers
+    // come from LDS reads.
     bf16x8 qf[16];
     {
-        bf16_t* sQ = smem + 2 * KTILE;                 // 64 KB: rows of 512 B
+        bf16_t* sQ = vslot(0);                         // 64 KB: rows of 512 B
         const bf16_t* qsrc = Q + (bh * S_pad + (long)blockIdx.x * QT) * HD;
         const __amdgpu_buffer_rsrc_t rQ = __builtin_amdgcn_make_buffer_rsrc((void*)qsrc, (short)0, QT * HD * 2, 0x00020000);
         // 128 rows x 32 chunks = 64 instructions of 1 KB, 16 per wave; lane -> row
@@ -124,6 +136,13 @@ void k_attention_bf16(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K
             int lc = (lane & 31) ^ (row & 31);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rQ, (lds_void*)(sQ + cb * 512), 16, (row * HD + lc * 8) * 2, 0, 0, 0);
         }
+        // K and the bias of tiles 0 and 1 go out meanwhile (their slots are not the Q stage)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) issue_k(j, 0, 0);
+        issue_b(0, 0);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) issue_k(j, 1, 1);
+        issue_b(1, 1);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         const int row = wave * 32 + l32;
@@ -131,6 +150,8 @@ void k_attention_bf16(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K
         for (int s = 0; s < 16; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(sQ + row * HD + (((2 * s + grp) ^ (row & 31)) * 8));
         __syncthreads();
     }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) issue_v(j, 0, 0);
 
     f32x16 o[8];
 #pragma unroll
@@ -138,28 +159,16 @@ void k_attention_bf16(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[t][r] = 0.f;
     float l_run = 0.f;
-    const float ref = REF_LOGIT * 1.4426950408889634f;
 
-    const int ntiles = (S + KT - 1) / KT;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) issue_k(j, 0, 0);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) issue_v(j, 0, 0);
-    issue_b(0, 0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
     // K rows this lane feeds to the S^T MFMA of sub-tile t: t*32 + swap23(lane & 31).
     const int krow0 = swap23(l32);
-    for (int kt = 0; kt < ntiles; ++kt) {
-        const int stage = kt & 1;
-        const bf16_t* sK = smem + stage * 2 * KTILE;
-        const bf16_t* sV = sK + KTILE;
-        const float* sB = reinterpret_cast<const float*>(smem + 4 * KTILE + (stage * 4 + wave) * 512);
+    constexpr int KD = 3;   // K fragments read KD k-steps ahead
+    constexpr int VD = 4;   // v^T fragments read VD MFMAs ahead
 
-        // ---- S^T starts at the key bias (0, or -inf for excluded keys); register
-        //      (t, i, j) of a lane holds key t*32 + (i/2)*16 + grp*8 + (i%2)*4 + j.
-        //      Read before the next tile's loads are issued (they target the other stage).
-        f32x16 st[2];
+    // S^T of the tile in K slot `ks` starts at its bias: register (t, i, j) of a
+    // lane holds key t*32 + (i/2)*16 + grp*8 + (i%2)*4 + j.
+    auto s_init = [&](f32x16* st, int ks) {
+        const float* sB = bslot(ks);
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -170,35 +179,86 @@ void k_attention_bf16(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K
                 st[t][i * 4 + 2] = bv.z;
                 st[t][i * 4 + 3] = bv.w;
             }
-        const int knext = min(kt + 1, ntiles - 1) * KT;   // key of the tile loaded during this one
+    };
+    auto kload = [&](const bf16_t* sK, int s, bf16x8* dst) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int row = t * 32 + krow0;
+            const int ch = (2 * s + grp) ^ kswz(row);
+            dst[t] = *reinterpret_cast<const bf16x8*>(sK + row * HD + ch * 8);
+        }
+    };
+    auto pack8 = [&](const float* pf) {
+        typedef float f32x8 __attribute__((ext_vector_type(8)));
+        const f32x8 v = {pf[0], pf[1], pf[2], pf[3], pf[4], pf[5], pf[6], pf[7]};
+        return __builtin_convertvector(v, bf16x8);
+    };
 
-        // ---- S^T += K Q^T: two independent 32-key chains; K fragments read three
-        //      k-steps ahead of their MFMAs.
-        constexpr int KD = 3;
+    // Prologue: S of tile 0 (K slot 0).
+    f32x16 sa[2], sb[2];
+    {
+        s_init(sa, 0);
+        const bf16_t* sK = kslot(0);
         bf16x8 kf[KD + 1][2];
-        auto kload = [&](int s, bf16x8* dst) {
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const int row = t * 32 + krow0;
-                const int ch = (2 * s + grp) ^ kswz(row);
-                dst[t] = *reinterpret_cast<const bf16x8*>(sK + row * HD + ch * 8);
-            }
-        };
-#pragma unroll
-        for (int s = 0; s < KD; ++s) kload(s, kf[s]);
+        for (int s = 0; s < KD; ++s) kload(sK, s, kf[s]);
 #pragma unroll
         for (int s = 0; s < 16; ++s) {
-            if (s + KD < 16) kload(s + KD, kf[(s + KD) % (KD + 1)]);
-            if ((s & 1) == 0) issue_k(s >> 1, knext, stage ^ 1);
+            if (s + KD < 16) kload(sK, s + KD, kf[(s + KD) % (KD + 1)]);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int t = 0; t < 2; ++t)
-                st[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s % (KD + 1)][t], qf[s], st[t], 0, 0, 0);
+                sa[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s % (KD + 1)][t], qf[s], sa[t], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
+    }
 
-        // ---- first v^T fragments go out before the exponentials
-        constexpr int VD = 4;
+    // Iteration t: `cur` holds S of tile t (complete), `nxt` receives S of tile t + 1.
+    auto iteration = [&](int t, f32x16* cur, f32x16* nxt) {
+        const int c = t & 1, n = c ^ 1;     // slots of tile t and tile t + 1
+        // every wave is past iteration t - 1: K slot c, v^T slot n and bias slot
+        // c are free; this wave's loads of K(t + 1), bias(t + 1) and v^T(t) landed
+        __builtin_amdgcn_s_waitcnt(0);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+
+        // ---- S(t + 1) = bias + K Q'^T with the exponentials of S(t) interleaved.
+        //      The bias is read before this iteration's first direct load is
+        //      issued (a read behind an LDS-writing load gets a full vmcnt wait).
+        s_init(nxt, n);
+        __builtin_amdgcn_sched_barrier(0);
+        const bf16_t* sK = kslot(n);
+        bf16x8 kf[KD + 1][2];
+#pragma unroll
+        for (int s = 0; s < KD; ++s) kload(sK, s, kf[s]);
+        bf16x8 pb[4];
+        float pf[8];
+        float psum = 0.f;
+#pragma unroll
+        for (int s = 0; s < 16; ++s) {
+            if (s + KD < 16) kload(sK, s + KD, kf[(s + KD) % (KD + 1)]);
+            if ((s & 1) == 0) issue_k(s >> 1, t + 2, c);
+            if (s == 1) issue_b(t + 2, c);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+                nxt[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s % (KD + 1)][u], qf[s], nxt[u], 0, 0, 0);
+            // p values 2 s and 2 s + 1 of S(t): key step s4 = s / 4, element e
+#pragma unroll
+            for (int q2 = 0; q2 < 2; ++q2) {
+                const int e = (2 * s + q2) & 7, s4 = s >> 2;
+                const int tt = s4 >> 1, i = 2 * (s4 & 1) + (e >> 2), j = e & 3;
+                pf[e] = __builtin_amdgcn_exp2f(cur[tt][i * 4 + j]);   // v_exp_f32; argument >= -48 or -inf
+                psum += pf[e];
+            }
+            if ((s & 3) == 3) pb[s >> 2] = pack8(pf);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        l_run += psum;
+
+        // ---- O^T += V^T P^T for tile t: 8 independent head-dim chains per key
+        //      step, v^T fragments read VD MFMAs ahead
+        const bf16_t* sV = vslot(c);
         bf16x8 vf[VD + 1];
         auto vload = [&](int idx, bf16x8& dst) {      // idx = s4 * 8 + ht
             const int s4 = idx >> 3, ht = idx & 7;
@@ -208,51 +268,22 @@ void k_attention_bf16(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K
         };
 #pragma unroll
         for (int x = 0; x < VD; ++x) vload(x, vf[x]);
-
-        // ---- P = exp2(S * log2(e)/16 - ref) for key step s4 (16 keys): the lane's
-        //      8 values are registers (t, i, j), t = s4/2, i in {2 (s4%2), +1}.
-        float psum = 0.f;
-        auto p_elem = [&](int s4, int e) {
-            const int t = s4 >> 1, i = 2 * (s4 & 1) + (e >> 2), j = e & 3;
-            return __builtin_amdgcn_exp2f(st[t][i * 4 + j] * scale_log2 - ref);   // v_exp_f32; argument >= -48 or -inf
-        };
-        auto pack8 = [&](const float* pf) {
-            union { bf16x8 v; uint32_t u[4]; } pk;
-#pragma unroll
-            for (int q2 = 0; q2 < 4; ++q2) pk.u[q2] = pack2bf(pf[2 * q2], pf[2 * q2 + 1]);
-            return pk.v;
-        };
-        bf16x8 pb[4];
-        {
-            float pf[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) pf[e] = p_elem(0, e), psum += pf[e];
-            pb[0] = pack8(pf);
-        }
-
-        // ---- O^T += V^T P^T: 8 independent head-dim chains per key step, v^T
-        //      fragments read four MFMAs ahead; the exponentials of key step
-        //      s4 + 1 are computed one per MFMA of step s4.
-        float pn[8];
 #pragma unroll
         for (int x = 0; x < 32; ++x) {
-            const int s4 = x >> 3, sub = x & 7;
             if (x + VD < 32) vload(x + VD, vf[(x + VD) % (VD + 1)]);
-            if ((x & 3) == 0) issue_v(x >> 2, knext, stage ^ 1);
-            if (x == 2) issue_b(knext, stage ^ 1);
+            if ((x & 3) == 0) issue_v(x >> 2, t + 1, n);
             __builtin_amdgcn_sched_barrier(0);
-            o[x & 7] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[x % (VD + 1)], pb[s4], o[x & 7], 0, 0, 0);
-            if (s4 + 1 < 4) {
-                pn[sub] = p_elem(s4 + 1, sub);
-                psum += pn[sub];
-                if (sub == 7) pb[s4 + 1] = pack8(pn);
-            }
+            o[x & 7] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[x % (VD + 1)], pb[x >> 3], o[x & 7], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
-        l_run += psum;
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+    };
+    int t = 0;
+    for (; t + 1 < ntiles; t += 2) {
+        iteration(t, sa, sb);
+        iteration(t + 1, sb, sa);
     }
+    if (t < ntiles) iteration(t, sa, sb);
+    __builtin_amdgcn_s_waitcnt(0);
 
     // ---- normalise and store: lane has query q0 + (lane & 31), head dims ht*32 + i*8 + 4 (lane>>5) + j
     const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
@@ -275,9 +306,8 @@ hipError_t attention_bf16(const bf16_t* q, const bf16_t* k, const bf16_t* vt, co
                           int S_pad, bf16_t* o, int d, hipStream_t s) {
     int S = g.S();
     if (g.B == 0 || S == 0) return hipSuccess;
-    const float scale_log2 = 1.4426950408889634f / 16.0f;  // log2(e) / sqrt(256)
     dim3 grid((S + QT - 1) / QT, H, g.B);
-    hipLaunchKernelGGL(k_attention_bf16, grid, dim3(256), 0, s, q, k, vt, bias, g, H, S_pad, o, d, scale_log2);
+    hipLaunchKernelGGL(k_attention_bf16, grid, dim3(256), 0, s, q, k, vt, bias, g, H, S_pad, o, d);
     return hipGetLastError();
 }
 

@@ -380,7 +380,7 @@ void k_gemm_bf16(GemmLaunch L) {
 #pragma unroll
                     for (int w = 0; w < WN; ++w) tot += rsum[w * 256 + lr], tsq += rsq[w * 256 + lr];
                     float mean = tot * (1.f / 256.f);
-                    float rstd = rsqrtf(tsq * (1.f / 256.f) + L.eps);
+                    float rstd = rsqrtf(tsq * (1.f / 256.f) + L.eps) * (which == 0 ? L.q_scale : 1.f);
 #pragma unroll
                     for (int nt = 0; nt < NT; ++nt)
                         st[lr * QS + lc_base + nt * 32] = f2bf((acc[mt][nt][r] - mean) * rstd);

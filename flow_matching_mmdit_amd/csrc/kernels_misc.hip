@@ -113,19 +113,95 @@ __global__ __launch_bounds__(256) void k_gemv(const float* __restrict__ x, int B
     }
 }
 
+// bf16 weights: each wave takes R rows at a time (all R x NI 16-byte weight
+// chunks of a lane requested before any arithmetic), so a wave keeps R rows of
+// weights in flight while the input vectors stay in registers.
+template <int BC, int NI, int R>
+__global__ __launch_bounds__(256) void k_gemv_bf16(const float* __restrict__ x, int B, int K,
+                                                   const bf16_t* __restrict__ W, int N,
+                                                   const bf16_t* __restrict__ bias, int silu_in,
+                                                   float* __restrict__ y, int b0) {
+    const int lane = threadIdx.x & 63;
+    const int nb = min(BC, B - b0);
+    float xr[NI][BC][8];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const int k0 = (lane + 64 * i) * 8;
+#pragma unroll
+        for (int b = 0; b < BC; ++b)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float v = 0.f;
+                if (b < nb && k0 + e < K) {
+                    v = x[(long)(b0 + b) * K + k0 + e];
+                    if (silu_in) v = silu_f(v);
+                }
+                xr[i][b][e] = v;
+            }
+    }
+    const int wave = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+    const int nwaves = (gridDim.x * blockDim.x) >> 6;
+    for (int n0 = wave * R; n0 < N; n0 += nwaves * R) {
+        uint4 w[R][NI];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                const int k0 = (lane + 64 * i) * 8;
+                w[r][i] = (n0 + r < N && k0 < K) ? *reinterpret_cast<const uint4*>(W + (long)(n0 + r) * K + k0)
+                                                 : make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            float acc[BC];
+#pragma unroll
+            for (int b = 0; b < BC; ++b) acc[b] = 0.f;
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                const uint32_t u[4] = {w[r][i].x, w[r][i].y, w[r][i].z, w[r][i].w};
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float lo = __uint_as_float(u[q] << 16), hi = __uint_as_float(u[q] & 0xFFFF0000u);
+#pragma unroll
+                    for (int b = 0; b < BC; ++b) acc[b] += lo * xr[i][b][2 * q] + hi * xr[i][b][2 * q + 1];
+                }
+            }
+#pragma unroll
+            for (int b = 0; b < BC; ++b) acc[b] = wave_sum(acc[b]);
+            const int n = n0 + r;
+            if (lane == 0 && n < N) {
+                const float bb = bias ? bf2f(bias[n]) : 0.f;
+                for (int b = 0; b < nb; ++b) y[(long)(b0 + b) * N + n] = acc[b] + bb;
+            }
+        }
+    }
+}
+
 hipError_t gemv(const float* x, int B, int K, const void* W, af_dtype wdt, int N, const void* bias,
                 int silu_in, float* y, hipStream_t s) {
     if (B == 0 || N == 0) return hipSuccess;
     constexpr int BC = 2;
-    int blocks = (N + 3) / 4;
-    if (blocks > 4096) blocks = 4096;
+    if (K > 4096) return hipErrorInvalidValue;
     for (int b0 = 0; b0 < B; b0 += BC) {
-        if (wdt == AF_BF16)
-            hipLaunchKernelGGL((k_gemv<bf16_t, BC, 8>), dim3(blocks), dim3(256), 0, s, x, B, K,
-                               (const bf16_t*)W, N, (const bf16_t*)bias, silu_in, y, b0);
-        else
+        if (wdt == AF_BF16) {
+            const int ni = (K + 511) / 512;
+            const bf16_t* Wb = (const bf16_t*)W;
+            const bf16_t* bb = (const bf16_t*)bias;
+#define AF_GEMV(NI, R)                                                                                       \
+    hipLaunchKernelGGL((k_gemv_bf16<BC, NI, R>), dim3(min((N + 4 * R - 1) / (4 * R), 2048)), dim3(256), 0, s, x, \
+                       B, K, Wb, N, bb, silu_in, y, b0)
+            if (ni <= 1) AF_GEMV(1, 4);
+            else if (ni <= 2) AF_GEMV(2, 4);
+            else if (ni <= 4) AF_GEMV(4, 4);
+            else if (ni <= 6) AF_GEMV(6, 4);
+            else AF_GEMV(8, 2);
+#undef AF_GEMV
+        } else {
+            int blocks = (N + 3) / 4;
+            if (blocks > 4096) blocks = 4096;
             hipLaunchKernelGGL((k_gemv<float, BC, 16>), dim3(blocks), dim3(256), 0, s, x, B, K,
                                (const float*)W, N, (const float*)bias, silu_in, y, b0);
+        }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -249,7 +325,7 @@ hipError_t f32_to_bf16(const float* src, bf16_t* dst, long n, hipStream_t s) {
 // Sequence position s of sample b: registers [0, R) always valid, text [R, Nt)
 // valid where mask[b, s - R] != 0, image [Nt, S) always valid, padding
 // [S, S_pad) never valid. Valid -> 0, excluded -> -inf.
-__global__ void k_key_bias(const uint8_t* __restrict__ mask, int T, int R, RowGeom g, int S_pad,
+__global__ void k_key_bias(const uint8_t* __restrict__ mask, int T, int R, RowGeom g, int S_pad, float keep,
                            float* __restrict__ bias) {
     long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= (long)g.B * S_pad) return;
@@ -258,14 +334,15 @@ __global__ void k_key_bias(const uint8_t* __restrict__ mask, int T, int R, RowGe
     if (s >= g.S()) valid = false;
     else if (s >= R && s < g.Nt) valid = mask == nullptr || mask[(long)b * T + (s - R)] != 0;
     else valid = true;
-    bias[i] = valid ? 0.f : -INFINITY;
+    bias[i] = valid ? keep : -INFINITY;
 }
 
-hipError_t key_bias(const uint8_t* mask, int T, int R, RowGeom g, int S_pad, float* bias, hipStream_t s) {
+hipError_t key_bias(const uint8_t* mask, int T, int R, RowGeom g, int S_pad, float keep, float* bias,
+                    hipStream_t s) {
     long n = (long)g.B * S_pad;
     if (n == 0) return hipSuccess;
     hipLaunchKernelGGL(k_key_bias, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, mask, T, R, g,
-                       S_pad, bias);
+                       S_pad, keep, bias);
     return hipGetLastError();
 }
 
@@ -283,34 +360,30 @@ template <> __device__ __forceinline__ void store4<float>(float* p, float a, flo
     *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
 }
 
-template <typename OT>
+template <typename OT, int MAXV>   // MAXV float4 per lane: d <= 256 MAXV
 __global__ __launch_bounds__(256) void k_ln_modulate(const float* __restrict__ x, int M, int d, RowGeom g,
                                                      int split, const float* __restrict__ mod,
                                                      long mod_stride, int sh_a, int sc_a, int sh_b,
                                                      int sc_b, OT* __restrict__ out, float eps) {
-    constexpr int MAXV = 16;  // float4 per lane -> d <= 4096
     const int lane = threadIdx.x & 63;
     const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (row >= M) return;
     const int nv = d / 4;
     const float* xr = x + (long)row * d;
     float4 v[MAXV];
-    float sum = 0.f;
 #pragma unroll
     for (int i = 0; i < MAXV; ++i) {
-        int c4 = lane + 64 * i;
-        if (c4 < nv) {
-            v[i] = reinterpret_cast<const float4*>(xr)[c4];
-            sum += (v[i].x + v[i].y) + (v[i].z + v[i].w);
-        } else {
-            v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-        }
+        const int c4 = lane + 64 * i;
+        v[i] = c4 < nv ? reinterpret_cast<const float4*>(xr)[c4] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i) sum += (v[i].x + v[i].y) + (v[i].z + v[i].w);
     const float mean = wave_sum(sum) / (float)d;
     float sq = 0.f;
 #pragma unroll
     for (int i = 0; i < MAXV; ++i) {
-        int c4 = lane + 64 * i;
+        const int c4 = lane + 64 * i;
         if (c4 < nv) {
             float a = v[i].x - mean, b = v[i].y - mean, c = v[i].z - mean, e = v[i].w - mean;
             sq += (a * a + b * b) + (c * c + e * e);
@@ -324,10 +397,10 @@ __global__ __launch_bounds__(256) void k_ln_modulate(const float* __restrict__ x
     OT* orow = out + (long)row * d;
 #pragma unroll
     for (int i = 0; i < MAXV; ++i) {
-        int c4 = lane + 64 * i;
+        const int c4 = lane + 64 * i;
         if (c4 < nv) {
-            float4 sh = reinterpret_cast<const float4*>(shp)[c4];
-            float4 sc = reinterpret_cast<const float4*>(scp)[c4];
+            const float4 sh = reinterpret_cast<const float4*>(shp)[c4];
+            const float4 sc = reinterpret_cast<const float4*>(scp)[c4];
             store4<OT>(orow + 4 * c4, (v[i].x - mean) * rstd * (1.f + sc.x) + sh.x,
                        (v[i].y - mean) * rstd * (1.f + sc.y) + sh.y,
                        (v[i].z - mean) * rstd * (1.f + sc.z) + sh.z,
@@ -336,17 +409,34 @@ __global__ __launch_bounds__(256) void k_ln_modulate(const float* __restrict__ x
     }
 }
 
+template <typename OT>
+static void launch_ln_modulate(int per_lane, dim3 grid, hipStream_t s, const float* x, int M, int d, RowGeom g,
+                               int split, const float* mod, long mod_stride, int sh_a, int sc_a, int sh_b, int sc_b,
+                               OT* out, float eps) {
+#define AF_LNM(V) hipLaunchKernelGGL((k_ln_modulate<OT, V>), grid, dim3(256), 0, s, x, M, d, g, split, mod, \
+                                     mod_stride, sh_a, sc_a, sh_b, sc_b, out, eps)
+    if (per_lane <= 1) AF_LNM(1);
+    else if (per_lane <= 2) AF_LNM(2);
+    else if (per_lane <= 4) AF_LNM(4);
+    else if (per_lane <= 8) AF_LNM(8);
+    else if (per_lane <= 12) AF_LNM(12);
+    else AF_LNM(16);
+#undef AF_LNM
+}
+
 hipError_t ln_modulate(const float* x, int M, int d, RowGeom g, int split, const float* mod, long mod_stride,
                        int sh_a, int sc_a, int sh_b, int sc_b, void* out, af_dtype odt, float eps,
                        hipStream_t s) {
     if (M == 0) return hipSuccess;
+    if (d % 4 != 0 || d > 4096) return hipErrorInvalidValue;
+    const int per_lane = (d / 4 + 63) / 64;
     dim3 grid((M + 3) / 4);
     if (odt == AF_BF16)
-        hipLaunchKernelGGL(k_ln_modulate<bf16_t>, grid, dim3(256), 0, s, x, M, d, g, split, mod, mod_stride,
-                           sh_a, sc_a, sh_b, sc_b, (bf16_t*)out, eps);
+        launch_ln_modulate<bf16_t>(per_lane, grid, s, x, M, d, g, split, mod, mod_stride, sh_a, sc_a, sh_b, sc_b,
+                                   (bf16_t*)out, eps);
     else
-        hipLaunchKernelGGL(k_ln_modulate<float>, grid, dim3(256), 0, s, x, M, d, g, split, mod, mod_stride,
-                           sh_a, sc_a, sh_b, sc_b, (float*)out, eps);
+        launch_ln_modulate<float>(per_lane, grid, s, x, M, d, g, split, mod, mod_stride, sh_a, sc_a, sh_b, sc_b,
+                                  (float*)out, eps);
     return hipGetLastError();
 }
 

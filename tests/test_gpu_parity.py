@@ -235,6 +235,9 @@ def test_block_pair_bf16_matches_oracle(af, block_pair):
     out = m.forward(*dev).cpu().numpy()
     torch.cuda.synchronize()
     for blk in (0, 1):
+        assert np.isfinite(taps[blk]).all()
+        bad = np.argwhere(~np.isfinite(got[blk]))
+        assert len(bad) == 0, (blk, len(bad), bad[:8].tolist())
         e, c = rel_max(got[blk], taps[blk]), cosine(got[blk], taps[blk])
         print(f"block {blk}: rel {e:.3e} cos {c:.6f}")
         assert e <= BF16_TOL and c >= BF16_COS, (blk, e, c)
