@@ -31,12 +31,14 @@
 // in its natural key order.
 //
 // Software pipeline (one wave per SIMD): iteration t runs the S MFMAs of tile
-// t + 1 with the exponentials of tile t interleaved (one MFMA, two p values),
-// then the P V MFMAs of tile t. K and v^T tiles have two LDS slots each, filled
+// t + 1 with the exponentials of tile t's first two key steps interleaved (one
+// per MFMA pair), then the P V MFMAs of tile t with the exponentials of its last
+// two key steps interleaved into the first half (one per MFMA). K and v^T tiles have two LDS slots each, filled
 // by gfx950 direct loads (buffer_load ... lds, 16 bytes per lane; the MUBUF form
-// keeps the compiler's LDS-read waits partial) that are spread over the MFMAs:
-// in iteration t, K and the bias of tile t + 2 and v^T of tile t + 1. One
-// barrier per iteration publishes them and frees the slots. 16-byte chunks are
+// keeps the compiler's LDS-read waits partial) issued one per S MFMA step: in
+// iteration t, K and the bias of tile t + 2 and v^T of tile t + 1, so each has
+// the whole P V phase to land before the next iteration's wait. One barrier per
+// iteration publishes them and frees the slots. 16-byte chunks are
 // XOR swizzled by row so both operand reads are bank-conflict free.
 #include "af_internal.h"
 
@@ -65,7 +67,9 @@ void k_attention_bf16(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K
     // bias block (4 copies of 64 fp32 keys)
     __shared__ __attribute__((aligned(1024))) bf16_t smem[4 * KTILE + 2 * 4 * 512];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // wave index in a scalar register: every LDS address a direct load takes (M0)
+    // is then formed with scalar arithmetic
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int grp = lane >> 5, l32 = lane & 31;
     const int b = blockIdx.z, h = blockIdx.y;
     const int S = g.S();
@@ -234,27 +238,29 @@ void k_attention_bf16(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K
         bf16x8 pb[4];
         float pf[8];
         float psum = 0.f;
+        // p value k (0..31) of S(t): key step s4 = k / 8, element e = k % 8
+        auto p_step = [&](int k) {
+            const int e = k & 7, s4 = k >> 3;
+            const int tt = s4 >> 1, i = 2 * (s4 & 1) + (e >> 2), j = e & 3;
+            pf[e] = __builtin_amdgcn_exp2f(cur[tt][i * 4 + j]);   // v_exp_f32; argument >= -48 or -inf
+            psum += pf[e];
+            if (e == 7) pb[s4] = pack8(pf);
+        };
 #pragma unroll
         for (int s = 0; s < 16; ++s) {
             if (s + KD < 16) kload(sK, s + KD, kf[(s + KD) % (KD + 1)]);
+            // this iteration's direct loads all go out during the S MFMAs, a
+            // whole P V phase ahead of the wait at the next iteration's barrier
             if ((s & 1) == 0) issue_k(s >> 1, t + 2, c);
-            if (s == 1) issue_b(t + 2, c);
+            else issue_v(s >> 1, t + 1, n);
+            if (s == 15) issue_b(t + 2, c);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int u = 0; u < 2; ++u)
                 nxt[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s % (KD + 1)][u], qf[s], nxt[u], 0, 0, 0);
-            // p values 2 s and 2 s + 1 of S(t): key step s4 = s / 4, element e
-#pragma unroll
-            for (int q2 = 0; q2 < 2; ++q2) {
-                const int e = (2 * s + q2) & 7, s4 = s >> 2;
-                const int tt = s4 >> 1, i = 2 * (s4 & 1) + (e >> 2), j = e & 3;
-                pf[e] = __builtin_amdgcn_exp2f(cur[tt][i * 4 + j]);   // v_exp_f32; argument >= -48 or -inf
-                psum += pf[e];
-            }
-            if ((s & 3) == 3) pb[s >> 2] = pack8(pf);
+            p_step(s);   // p values 0..15 (key steps 0, 1) during the S MFMAs
             __builtin_amdgcn_sched_barrier(0);
         }
-        l_run += psum;
 
         // ---- O^T += V^T P^T for tile t: 8 independent head-dim chains per key
         //      step, v^T fragments read VD MFMAs ahead
@@ -271,11 +277,12 @@ void k_attention_bf16(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K
 #pragma unroll
         for (int x = 0; x < 32; ++x) {
             if (x + VD < 32) vload(x + VD, vf[(x + VD) % (VD + 1)]);
-            if ((x & 3) == 0) issue_v(x >> 2, t + 1, n);
             __builtin_amdgcn_sched_barrier(0);
             o[x & 7] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[x % (VD + 1)], pb[x >> 3], o[x & 7], 0, 0, 0);
+            if (x < 16) p_step(16 + x);   // p values 16..31 (key steps 2, 3) before their MFMAs
             __builtin_amdgcn_sched_barrier(0);
         }
+        l_run += psum;
     };
     int t = 0;
     for (; t + 1 < ntiles; t += 2) {

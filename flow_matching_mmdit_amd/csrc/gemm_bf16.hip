@@ -89,7 +89,9 @@ void k_gemm_bf16(GemmLaunch L) {
     static_assert(((BM / RPI) / NW) % 2 == 0, "per-wave load count must be even");
     __shared__ __attribute__((aligned(1024))) bf16_t smem[SMEM_ELEMS];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // wave index in a scalar register: the LDS addresses of the direct loads (M0)
+    // are then formed with scalar arithmetic
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WN, wn = wave % WN;
     const int tiles_n = L.N / BN;
 
