@@ -61,6 +61,11 @@ __device__ __forceinline__ int swz(int row) { return ((row >> 1) ^ (row >> 3)) &
 // outstanding (expcnt and lgkmcnt left unconstrained).
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 __host__ __device__ __forceinline__ int tiles_m(int M) { return (M + BM - 1) / BM; }
+// MFMA operand order of a tile: false -> acc = A W^T (a lane holds one column and
+// four consecutive rows per 4-register group), true -> acc = (W A^T) = C^T (a lane
+// holds one row and four consecutive columns), for epilogues that reduce or store
+// along rows.
+template <bool T> struct Orient { static constexpr bool value = T; };
 
 // Issues this wave's share of one 256 x BK operand sub-tile: the sub-tile is
 // 256 / RPI blocks of 1 KB (RPI rows each); with NW waves, wave w issues blocks
@@ -160,12 +165,16 @@ void k_gemm_bf16(GemmLaunch L) {
             b[nt] = *reinterpret_cast<const bf16x8*>(sB + r * BK + c * 8);
         }
     };
-    auto mfmas = [&](const bf16x8* a, const bf16x8* b) {
+    auto mfmas = [&](const bf16x8* a, const bf16x8* b, auto orient) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-                acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mt], b[nt], acc[mt][nt], 0, 0, 0);
+            for (int nt = 0; nt < NT; ++nt) {
+                if constexpr (decltype(orient)::value)
+                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[nt], a[mt], acc[mt][nt], 0, 0, 0);
+                else
+                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mt], b[nt], acc[mt][nt], 0, 0, 0);
+            }
     };
     // Issue order inside a k-step: the fragment reads for the next k-step, then
     // the MFMAs with the k-step's direct loads slotted in after the first and the
@@ -200,46 +209,62 @@ void k_gemm_bf16(GemmLaunch L) {
     auto issueW = [&](int t, int st) {
         issue_tile<NW>(rW, woff, min(t, KT - 1) * BK * 2, ldwb, slot_ptr(st) + TILE_ELEMS, wave);
     };
-#pragma unroll
-    for (int t = 0; t < NS - 2; ++t) {
-        issueA(t, t);
-        issueW(t, t);
-    }
-    issueA(NS - 2, NS - 2);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER2 * (NS - 3) + PER));   // sub-tile 0 landed
-    __builtin_amdgcn_s_barrier();
-    bf16x8 fa0[MT], fb0[NT], fa1[MT], fb1[NT];
-    load_frags(slot_ptr(0), slot_ptr(0) + TILE_ELEMS, 0, fa0, fb0);
-    int cs = 0;
-    for (int j = 0; j < KT; ++j) {
-        const bf16_t* cur = slot_ptr(cs);
-        const int ns = cs + 1 == NS ? 0 : cs + 1;      // slot of j + 1
-        const int fs = cs == 0 ? NS - 1 : cs - 1;      // slot of j - 1
-        const int f2 = fs == 0 ? NS - 1 : fs - 1;      // slot of j - 2
-        issueW(j + NS - 2, f2);
-        load_frags(cur, cur + TILE_ELEMS, 1, fa1, fb1);
-        mfmas(fa0, fb0);
-        pattern();
-        __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER2 * (NS - 3)) & ~(15 << 8));   // and lgkmcnt(0)
+    auto mainloop = [&](auto orient) {
+    #pragma unroll
+        for (int t = 0; t < NS - 2; ++t) {
+            issueA(t, t);
+            issueW(t, t);
+        }
+        issueA(NS - 2, NS - 2);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER2 * (NS - 3) + PER));   // sub-tile 0 landed
         __builtin_amdgcn_s_barrier();
-        __builtin_amdgcn_sched_barrier(0);
-        issueA(j + NS - 1, fs);
-        const bf16_t* nxt = slot_ptr(ns);
-        load_frags(nxt, nxt + TILE_ELEMS, 0, fa0, fb0);
-        mfmas(fa1, fb1);
-        pattern();
-        __builtin_amdgcn_sched_barrier(0);
-        cs = ns;
+        bf16x8 fa0[MT], fb0[NT], fa1[MT], fb1[NT];
+        load_frags(slot_ptr(0), slot_ptr(0) + TILE_ELEMS, 0, fa0, fb0);
+        int cs = 0;
+        for (int j = 0; j < KT; ++j) {
+            const bf16_t* cur = slot_ptr(cs);
+            const int ns = cs + 1 == NS ? 0 : cs + 1;      // slot of j + 1
+            const int fs = cs == 0 ? NS - 1 : cs - 1;      // slot of j - 1
+            const int f2 = fs == 0 ? NS - 1 : fs - 1;      // slot of j - 2
+            issueW(j + NS - 2, f2);
+            load_frags(cur, cur + TILE_ELEMS, 1, fa1, fb1);
+            mfmas(fa0, fb0, orient);
+            pattern();
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER2 * (NS - 3)) & ~(15 << 8));   // and lgkmcnt(0)
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            issueA(j + NS - 1, fs);
+            const bf16_t* nxt = slot_ptr(ns);
+            load_frags(nxt, nxt + TILE_ELEMS, 0, fa0, fb0);
+            mfmas(fa1, fb1, orient);
+            pattern();
+            __builtin_amdgcn_sched_barrier(0);
+            cs = ns;
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    };
+    // q and k tiles of the QKV GEMM and the SwiGLU tiles run in the row-major
+    // (C^T) orientation; everything else in the column-major one.
+    if constexpr (EPI == EPI_SWIGLU) {
+        mainloop(Orient<true>{});
+    } else if constexpr (EPI == EPI_QKV) {
+        if (n0 / (L.N / 3) < 2) mainloop(Orient<true>{});
+        else mainloop(Orient<false>{});
+    } else {
+        mainloop(Orient<false>{});
     }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
 
     // ---------------------------------------------------------------- epilogues
-    // acc[mt][nt][i*4+j] holds row wm*128 + mt*32 + i*8 + (lane>>5)*4 + j,
-    // column wn*128 + nt*32 + (lane&31) of the block tile. LDS is free here.
+    // Column-major orientation: acc[mt][nt][i*4+j] holds row wm*64 + mt*32 + i*8 +
+    // (lane>>5)*4 + j, column wn*128 + nt*32 + (lane&31) of the block tile.
+    // Row-major orientation: acc[mt][nt][i*4+j] holds row wm*64 + mt*32 + (lane&31),
+    // column wn*128 + nt*32 + i*8 + (lane>>5)*4 + j. LDS is free here.
     const int lr_base = wm * TM + (lane >> 5) * 4;
     const int lc_base = wn * TN + (lane & 31);
+    const int rr_row = wm * TM + (lane & 31);           // row-major: row of mt = 0
+    const int rr_col = wn * TN + (lane >> 5) * 4;       // row-major: column of nt = i = j = 0
 
     if constexpr (EPI == EPI_STORE) {
         bf16_t* C = (bf16_t*)L.C;
@@ -307,18 +332,21 @@ void k_gemm_bf16(GemmLaunch L) {
         }
     } else if constexpr (EPI == EPI_SWIGLU) {
         // h tile [256 rows][128 cols] bf16 staged in LDS, then 16-byte row stores.
+        // Row-major orientation: gate block nt = 2p and up block 2p + 1 give h
+        // columns wn*64 + p*32 + i*8 + grp*4 + j, four of them per 8-byte write.
         bf16_t* st = smem;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                int lr = lr_base + mt * 32 + (r >> 2) * 8 + (r & 3);
+            for (int p2 = 0; p2 < NT / 2; ++p2)
 #pragma unroll
-                for (int p2 = 0; p2 < NT / 2; ++p2) {
-                    float gt = acc[mt][2 * p2][r], up = acc[mt][2 * p2 + 1][r];
-                    st[lr * HS + wn * (TN / 2) + p2 * 32 + (lane & 31)] = f2bf(silu_f(gt) * up);
+                for (int i = 0; i < 4; ++i) {
+                    float h[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) h[j] = silu_f(acc[mt][2 * p2][i * 4 + j]) * acc[mt][2 * p2 + 1][i * 4 + j];
+                    *reinterpret_cast<uint2*>(st + (rr_row + mt * 32) * HS + wn * (TN / 2) + p2 * 32 + i * 8 +
+                                              (lane >> 5) * 4) = make_uint2(pack2bf(h[0], h[1]), pack2bf(h[2], h[3]));
                 }
-            }
         __syncthreads();
         bf16_t* Hout = (bf16_t*)L.C;
         const int fcol0 = n0 / 2;
@@ -342,51 +370,59 @@ void k_gemm_bf16(GemmLaunch L) {
         float* rsum = reinterpret_cast<float*>(smem + 256 * QS);   // [WN][256]
         float* rsq = rsum + WN * 256;                               // [WN][256]
         if (which < 2) {
-            // Per-row LayerNorm over the 256 head columns, split across the two wn waves.
+            // Row-major orientation: per-row LayerNorm over the 256 head columns;
+            // each lane sums its 64 values of a row, the lane holding the other
+            // half-wave's 64 adds in, and the two wn waves meet through LDS.
+            float mean[MT], rstd[MT];
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
+            for (int mt = 0; mt < MT; ++mt) {
+                float s1 = 0.f;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float s = 0.f;
+                for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-                    for (int nt = 0; nt < NT; ++nt) s += acc[mt][nt][r];
-                    s = half_wave_sum(s);
-                    if ((lane & 31) == 0) rsum[wn * 256 + lr_base + mt * 32 + (r >> 2) * 8 + (r & 3)] = s;
-                }
+                    for (int r = 0; r < 16; ++r) s1 += acc[mt][nt][r];
+                s1 += __shfl_xor(s1, 32, 64);
+                if ((lane >> 5) == 0) rsum[wn * 256 + rr_row + mt * 32] = s1;
+            }
             __syncthreads();
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
+            for (int mt = 0; mt < MT; ++mt) {
+                float tot = 0.f;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    int lr = lr_base + mt * 32 + (r >> 2) * 8 + (r & 3);
-                    float tot = 0.f;
+                for (int w = 0; w < WN; ++w) tot += rsum[w * 256 + rr_row + mt * 32];
+                mean[mt] = tot * (1.f / 256.f);
+                float s2 = 0.f;
 #pragma unroll
-                    for (int w = 0; w < WN; ++w) tot += rsum[w * 256 + lr];
-                    float mean = tot * (1.f / 256.f);
-                    float s = 0.f;
+                for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-                    for (int nt = 0; nt < NT; ++nt) {
-                        float c = acc[mt][nt][r] - mean;
-                        s += c * c;
+                    for (int r = 0; r < 16; ++r) {
+                        const float c = acc[mt][nt][r] - mean[mt];
+                        s2 += c * c;
                     }
-                    s = half_wave_sum(s);
-                    if ((lane & 31) == 0) rsq[wn * 256 + lr] = s;
-                }
+                s2 += __shfl_xor(s2, 32, 64);
+                if ((lane >> 5) == 0) rsq[wn * 256 + rr_row + mt * 32] = s2;
+            }
             __syncthreads();
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                float tsq = 0.f;
+#pragma unroll
+                for (int w = 0; w < WN; ++w) tsq += rsq[w * 256 + rr_row + mt * 32];
+                rstd[mt] = rsqrtf(tsq * (1.f / 256.f) + L.eps) * (which == 0 ? L.q_scale : 1.f);
+            }
+            // normalised tile -> LDS, four consecutive columns per 8-byte write
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    int lr = lr_base + mt * 32 + (r >> 2) * 8 + (r & 3);
-                    float tot = 0.f, tsq = 0.f;
+                for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-                    for (int w = 0; w < WN; ++w) tot += rsum[w * 256 + lr], tsq += rsq[w * 256 + lr];
-                    float mean = tot * (1.f / 256.f);
-                    float rstd = rsqrtf(tsq * (1.f / 256.f) + L.eps) * (which == 0 ? L.q_scale : 1.f);
+                    for (int i = 0; i < 4; ++i) {
+                        float v[4];
 #pragma unroll
-                    for (int nt = 0; nt < NT; ++nt)
-                        st[lr * QS + lc_base + nt * 32] = f2bf((acc[mt][nt][r] - mean) * rstd);
-                }
+                        for (int j = 0; j < 4; ++j) v[j] = (acc[mt][nt][i * 4 + j] - mean[mt]) * rstd[mt];
+                        *reinterpret_cast<uint2*>(st + (rr_row + mt * 32) * QS + rr_col + nt * 32 + i * 8) =
+                            make_uint2(pack2bf(v[0], v[1]), pack2bf(v[2], v[3]));
+                    }
             __syncthreads();
             // rows -> [B, H, S_pad, 256]: 32 chunks of 16 B per row
             bf16_t* dst = (bf16_t*)(which == 0 ? L.q : L.k);
