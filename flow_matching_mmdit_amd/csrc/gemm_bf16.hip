@@ -54,9 +54,12 @@ static_assert(SMEM_ELEMS >= 2 * NS * TILE_ELEMS, "operand slots exceed the LDS b
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Chunk swizzle per row (4 chunks of 16 B per 64-byte row) so the 32 rows one
-// MFMA operand read touches spread over all banks.
-__device__ __forceinline__ int swz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+// Chunk swizzle per row (4 chunks of 16 B per 64-byte row). Rows r and r + 4
+// start on the same bank, so the chunk is XORed with bits 2..3 of the row: the
+// MFMA operand reads (ds_read_b128) then run conflict free (measured with the
+// LDS bank-conflict counter; an XOR with bits 1 and 3 still gave two-way
+// conflicts on gfx950).
+__device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
 // s_waitcnt immediate that waits until at most n vector-memory operations are
 // outstanding (expcnt and lgkmcnt left unconstrained).
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
@@ -70,10 +73,10 @@ template <bool T> struct Orient { static constexpr bool value = T; };
 // Issues this wave's share of one 256 x BK operand sub-tile: the sub-tile is
 // 256 / RPI blocks of 1 KB (RPI rows each); with NW waves, wave w issues blocks
 // cb = w * PER + j. Lane l fills physical chunk l % CH of row RPI cb + l / CH
-// with logical chunk (l % CH) ^ swz(row). swz depends on cb only through its
-// parity, so two per-lane byte offsets (voff[j & 1]) plus a uniform row step
-// (in the scalar offset, with the sub-tile's k offset `sbase`) cover all of the
-// wave's instructions.
+// with logical chunk (l % CH) ^ swz(row). swz depends on the row only within
+// its 16-row block, so per-lane byte offsets for two blocks (voff[j & 1]) plus a
+// uniform row step (in the scalar offset, with the sub-tile's k offset `sbase`)
+// cover all of the wave's instructions.
 template <int NW>
 __device__ __forceinline__ void issue_tile(__amdgpu_buffer_rsrc_t rsrc, const uint32_t* voff, int sbase, int ldbytes,
                                            bf16_t* lds_tile, int wave) {
