@@ -8,7 +8,10 @@ drawn from the seeded synthetic recipe. One step = one full forward through the
 C-ABI (every kernel of the path), inputs already resident in HBM.
 
 Prints one JSON line. The timed region is bracketed by synchronisation and
-measured with HIP events on the stream the kernels run on.
+measured with HIP events on the forward's stream; with two sample groups (the
+default) the batch halves run on two concurrent streams forked from and joined
+back into that stream. The per-kernel pass (roofline, per-class times) runs the
+batch as one group so that launches do not overlap.
 """
 import argparse
 import json
@@ -120,6 +123,8 @@ def main():
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default="1024")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true")
+    ap.add_argument("--groups", type=int, choices=(1, 2), default=2,
+                    help="sample groups of the timed forwards (2: the batch halves run on two concurrent streams)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the forward runs on a single MI355X and this build has no "
@@ -160,29 +165,51 @@ def main():
     mask = torch.from_numpy(seeded_inputs.length_mask(seeded_inputs.valid_lengths(B, 16, T), T)).cuda()
     out = torch.empty((B, 4, H, W), dtype=torch.float32, device="cuda")
 
+    def check_finite(where):
+        bad = (~torch.isfinite(out)).reshape(B, -1).sum(1).tolist()
+        assert sum(bad) == 0, f"non-finite output after {where}: per-sample counts {bad}"
+
+    model.set_sample_groups(args.groups)
     for _ in range(args.warmup):
         model.forward(lat, tau, text, mask, out=out)
     torch.cuda.synchronize()
+    check_finite("warm-up")
     print(f"[bench] warmup done", file=sys.stderr, flush=True)
 
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(args.steps):
-        model.forward(lat, tau, text, mask, out=out)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1)
-    ms_per_step = ms / args.steps
+
+    def timed(n):
+        # the forward forks from and joins back into `stream`, so events on it
+        # bracket all of its work
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(n):
+            model.forward(lat, tau, text, mask, out=out)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    ms_per_step = timed(args.steps)
     value = 1000.0 / ms_per_step
     flops = forward_flops(d, F, L, B, S, T, cfg.joint_attention_dim, Nimg, 16)
     tflops = flops / (ms_per_step * 1e-3) / 1e12
-    assert torch.isfinite(out).all().item(), "non-finite output"
+    check_finite("the timed forwards")
     print(f"[bench] {ms_per_step:.2f} ms/forward, {tflops:.1f} TFLOP/s", file=sys.stderr, flush=True)
+
+    # The whole batch as one group, for comparison and for the per-kernel pass
+    # (launches of two groups overlap in time, so their durations would not be
+    # the kernels' own).
+    ms_one_group = ms_per_step
+    if args.groups != 1:
+        model.set_sample_groups(1)
+        model.forward(lat, tau, text, mask, out=out)
+        ms_one_group = timed(args.steps)
+        print(f"[bench] one group: {ms_one_group:.2f} ms/forward", file=sys.stderr, flush=True)
 
     kernels, roofline = {}, None
     if not args.no_profile:
+        model.set_sample_groups(1)
         af.af_profile(model, True)
         for _ in range(args.steps):
             model.forward(lat, tau, text, mask, out=out)
@@ -246,6 +273,8 @@ def main():
         "tflops": tflops,
         "pct_peak_bf16": 100.0 * tflops / PEAK_BF16_TFLOPS,
         "flops_per_forward": flops,
+        "sample_groups": args.groups,
+        "ms_per_step_one_group": ms_one_group,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels": kernels,

@@ -167,6 +167,12 @@ struct af_model {
     size_t staging_floats = 0;
     void* work = nullptr;
 
+    // Sample groups run concurrently: group 0 on the caller's stream, group 1 on
+    // `side` (default priority, non-blocking), forked and joined with events.
+    int groups = 2;
+    hipStream_t side = nullptr;
+    hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+
     // per-kernel-class event timing (af_profile)
     bool prof_on = false;
     struct Rec { hipEvent_t a, b; int cls; };
@@ -365,14 +371,14 @@ af_status gemm(af_model* m, GemmLaunch& L, hipStream_t s) {
         if (s_ != AF_OK) return s_;     \
     } while (0)
 
-GemmLaunch gemm_base(af_model* m, RowGeom g, int N, int K, int epi) {
+GemmLaunch gemm_base(af_model* m, const float* mod, RowGeom g, int N, int K, int epi) {
     GemmLaunch L;
     memset(&L, 0, sizeof(L));
     L.N = N;
     L.K = K;
     L.epi = epi;
     L.geom = g;
-    L.mod = m->mod;
+    L.mod = mod;
     L.mod_stride = m->D.mod_cols;
     L.H = m->D.H;
     L.hd = m->D.hd;
@@ -381,10 +387,38 @@ GemmLaunch gemm_base(af_model* m, RowGeom g, int N, int K, int epi) {
     return L;
 }
 
+// The activation buffers of one group of samples [b0, b0 + B): each group keeps
+// the whole-batch row layout ([text rows of its samples][image rows of its
+// samples]) in its own row range, and its own slices of the per-sample buffers.
+struct View {
+    float* resid;
+    void *nrm, *attn, *ffh, *q, *k, *v;
+    float *raw, *kbias, *mod;
+};
+
+View group_view(af_model* m, int b0, int S, int S_pad) {
+    const Derived& D = m->D;
+    const size_t es = m->es;
+    const long r0 = (long)b0 * S;                                    // first row of the group
+    const size_t qkv = (size_t)b0 * D.H * S_pad * D.hd * es;         // bytes before the group's q/k/v
+    View V;
+    V.resid = m->resid + r0 * D.d;
+    V.nrm = (char*)m->nrm + r0 * D.d * es;
+    V.attn = (char*)m->attn + r0 * D.d * es;
+    V.ffh = (char*)m->ffh + r0 * D.F * es;
+    V.q = (char*)m->q + qkv;
+    V.k = (char*)m->k + qkv;
+    V.v = (char*)m->v + qkv;
+    V.raw = m->raw ? m->raw + r0 * std::max(3 * D.d, 2 * D.F) : nullptr;
+    V.kbias = m->kbias + (size_t)b0 * S_pad;
+    V.mod = m->mod + (size_t)b0 * D.mod_cols;
+    return V;
+}
+
 // One transformer block. Streams: 2 for a joint block (text rows then image
 // rows, each with its own weights and modulation), 1 for a single block.
-af_status run_block(af_model* m, RowGeom g, int S_pad, const BlockW* wt, const BlockW* wi, long off_t, long off_i,
-                    hipStream_t s) {
+af_status run_block(af_model* m, const View& V, RowGeom g, int S_pad, const BlockW* wt, const BlockW* wi, long off_t,
+                    long off_i, hipStream_t s) {
     const Derived& D = m->D;
     const long d = D.d, F = D.F;
     const int M = g.B * g.S();
@@ -416,64 +450,133 @@ af_status run_block(af_model* m, RowGeom g, int S_pad, const BlockW* wt, const B
     // 1. LN + modulate(shift1, scale1)
     {
     ProfScope ps(m, AF_K_LN_MOD, s);
-    AF_K(ln_modulate(m->resid, M, d, g, split, m->mod, D.mod_cols, off_a, off_a + d, off_b, off_b + d, m->nrm, m->dt,
+    AF_K(ln_modulate(V.resid, M, d, g, split, V.mod, D.mod_cols, off_a, off_a + d, off_b, off_b + d, V.nrm, m->dt,
                      m->cfg.ln_eps, s));
     }
     // 2. QKV (+ QK-norm)
     {
         ProfScope ps(m, AF_K_GEMM_QKV, s);
-        GemmLaunch L = gemm_base(m, g, 3 * d, d, m->dt == AF_BF16 ? EPI_QKV : EPI_STORE);
-        L.q = m->q; L.k = m->k; L.vt = m->v; L.S_pad = S_pad;
+        GemmLaunch L = gemm_base(m, V.mod, g, 3 * d, d, m->dt == AF_BF16 ? EPI_QKV : EPI_STORE);
+        L.q = V.q; L.k = V.k; L.vt = V.v; L.S_pad = S_pad;
         L.q_scale = ATTN_BF16_Q_SCALE;
-        L.C = m->raw; L.ldc = 3 * d;
-        add_groups(L, (const char*)m->nrm, d, d * es, 0, 0);
+        L.C = V.raw; L.ldc = 3 * d;
+        add_groups(L, (const char*)V.nrm, d, d * es, 0, 0);
         AF_TRY(gemm(m, L, s));
         if (m->dt == AF_F32)
-            AF_K(qknorm_scatter_f32(m->raw, M, g, D.H, D.hd, S_pad, m->cfg.ln_eps, (float*)m->q, (float*)m->k,
-                                    (float*)m->v, 0, s));
+            AF_K(qknorm_scatter_f32(V.raw, M, g, D.H, D.hd, S_pad, m->cfg.ln_eps, (float*)V.q, (float*)V.k,
+                                    (float*)V.v, 0, s));
     }
     // 3. attention over [registers; text; image]
     {
     ProfScope ps(m, AF_K_ATTENTION, s);
     if (m->dt == AF_BF16)
-        AF_K(attention_bf16((const bf16_t*)m->q, (const bf16_t*)m->k, (const bf16_t*)m->v, m->kbias, g, D.H, S_pad,
-                            (bf16_t*)m->attn, d, s));
+        AF_K(attention_bf16((const bf16_t*)V.q, (const bf16_t*)V.k, (const bf16_t*)V.v, V.kbias, g, D.H, S_pad,
+                            (bf16_t*)V.attn, d, s));
     else
-        AF_K(attention_f32((const float*)m->q, (const float*)m->k, (const float*)m->v, m->kbias, g, D.H, D.hd, S_pad,
-                           (float*)m->attn, d, s));
+        AF_K(attention_f32((const float*)V.q, (const float*)V.k, (const float*)V.v, V.kbias, g, D.H, D.hd, S_pad,
+                           (float*)V.attn, d, s));
     }
     // 4. out projection, residual += gate1 * (.)
     {
         ProfScope ps(m, AF_K_GEMM_OUT, s);
-        GemmLaunch L = gemm_base(m, g, d, d, EPI_GATED_RESID);
-        L.resid = m->resid;
-        add_groups(L, (const char*)m->attn, d, d * es, 1, 2 * d);
+        GemmLaunch L = gemm_base(m, V.mod, g, d, d, EPI_GATED_RESID);
+        L.resid = V.resid;
+        add_groups(L, (const char*)V.attn, d, d * es, 1, 2 * d);
         AF_TRY(gemm(m, L, s));
     }
     // 5. LN + modulate(shift2, scale2)
     {
     ProfScope ps(m, AF_K_LN_MOD, s);
-    AF_K(ln_modulate(m->resid, M, d, g, split, m->mod, D.mod_cols, off_a + 3 * d, off_a + 4 * d, off_b + 3 * d,
-                     off_b + 4 * d, m->nrm, m->dt, m->cfg.ln_eps, s));
+    AF_K(ln_modulate(V.resid, M, d, g, split, V.mod, D.mod_cols, off_a + 3 * d, off_a + 4 * d, off_b + 3 * d,
+                     off_b + 4 * d, V.nrm, m->dt, m->cfg.ln_eps, s));
     }
     // 6. FFN up: silu(gate) * up
     {
         ProfScope ps(m, AF_K_GEMM_FFN_UP, s);
-        GemmLaunch L = gemm_base(m, g, 2 * F, d, m->dt == AF_BF16 ? EPI_SWIGLU : EPI_STORE);
-        if (m->dt == AF_BF16) { L.C = m->ffh; L.ldc = F; }
-        else { L.C = m->raw; L.ldc = 2 * F; }
-        add_groups(L, (const char*)m->nrm, d, d * es, 2, 0);
+        GemmLaunch L = gemm_base(m, V.mod, g, 2 * F, d, m->dt == AF_BF16 ? EPI_SWIGLU : EPI_STORE);
+        if (m->dt == AF_BF16) { L.C = V.ffh; L.ldc = F; }
+        else { L.C = V.raw; L.ldc = 2 * F; }
+        add_groups(L, (const char*)V.nrm, d, d * es, 2, 0);
         AF_TRY(gemm(m, L, s));
-        if (m->dt == AF_F32) AF_K(swiglu_f32(m->raw, M, F, (float*)m->ffh, s));
+        if (m->dt == AF_F32) AF_K(swiglu_f32(V.raw, M, F, (float*)V.ffh, s));
     }
     // 7. FFN down, residual += gate2 * (.)
     {
         ProfScope ps(m, AF_K_GEMM_FFN_DOWN, s);
-        GemmLaunch L = gemm_base(m, g, d, F, EPI_GATED_RESID);
-        L.resid = m->resid;
-        add_groups(L, (const char*)m->ffh, F, F * es, 3, 5 * d);
+        GemmLaunch L = gemm_base(m, V.mod, g, d, F, EPI_GATED_RESID);
+        L.resid = V.resid;
+        add_groups(L, (const char*)V.ffh, F, F * es, 3, 5 * d);
         AF_TRY(gemm(m, L, s));
     }
+    return AF_OK;
+}
+
+// Samples [b0, b0 + Bg) of a forward whose per-sample prologue (key bias,
+// modulation vectors, bf16 text) is already on the device: embeddings, the
+// blocks and the final layer (or a residual tap) on stream s.
+af_status run_group(af_model* m, const Inputs& in, int b0, int Bg, int stop_after, float* resid_out, float* out,
+                    hipStream_t s) {
+    const Derived& D = m->D;
+    const af_config& c = m->cfg;
+    const long d = D.d;
+    const int p = c.patch_size;
+    const int h = in.H / p, w = in.W / p;
+    RowGeom g{Bg, D.R + in.T, h * w};
+    const int S = g.S();
+    const int S_pad = (S + 127) / 128 * 128;
+    const View V = group_view(m, b0, S, S_pad);
+    const size_t pix = (size_t)in.H * in.W;
+
+    ProfScope ps_embed(m, AF_K_EMBED, s);
+    // embeddings: image rows, register rows, caption rows
+    AF_K(patch_embed(in.latents + (size_t)b0 * c.in_channels * pix, c.in_channels, in.H, in.W, p, m->pe_w, m->pe_b,
+                     m->dt, m->pos, D.G, V.resid, g, d, s));
+    AF_K(copy_registers(m->reg, m->dt, D.R, V.resid, g, d, s));
+    if (in.T > 0) {
+        // bf16 models read the staged bf16 copy; fp32 models take fp32 text
+        const size_t first = (size_t)b0 * in.T * c.joint_attention_dim;
+        const void* text = m->dt == AF_BF16 ? (const void*)(m->text_bf16 + first)
+                                            : (const void*)((const float*)in.text + first);
+        GemmLaunch L = gemm_base(m, V.mod, g, d, c.joint_attention_dim, EPI_STORE_MAPPED);
+        L.resid = V.resid;
+        L.seg_len = in.T;
+        L.seg_stride = g.Nt;
+        L.seg_off = D.R;
+        L.ngroups = 1;
+        L.g[0].A = text;
+        L.g[0].lda = c.joint_attention_dim;
+        L.g[0].W = m->ctx_w;
+        L.g[0].ldw = c.joint_attention_dim;
+        L.g[0].M = Bg * in.T;
+        AF_TRY(gemm(m, L, s));
+    }
+    ps_embed.end();
+    float* tap = resid_out ? resid_out + (size_t)b0 * S * d : nullptr;
+    if (stop_after == -1) {
+        AF_K(taps_permute(V.resid, g, d, tap, s));
+        return AF_OK;
+    }
+    int bi = 0;
+    for (int j = 0; j < D.Lj; ++j, ++bi) {
+        AF_TRY(run_block(m, V, g, S_pad, &m->joint_txt[j], &m->joint_img[j], (long)(2 * j + 1) * 6 * d,
+                         (long)(2 * j) * 6 * d, s));
+        if (stop_after == bi) {
+            AF_K(taps_permute(V.resid, g, d, tap, s));
+            return AF_OK;
+        }
+    }
+    for (int i = 0; i < D.Ls; ++i, ++bi) {
+        AF_TRY(run_block(m, V, g, S_pad, &m->single[i], nullptr, (long)(2 * D.Lj + i) * 6 * d, 0, s));
+        if (stop_after == bi) {
+            AF_K(taps_permute(V.resid, g, d, tap, s));
+            return AF_OK;
+        }
+    }
+    // pre-final modulation (scale, shift) + projection + unpatchify
+    const long foff = (long)(2 * D.Lj + D.Ls) * 6 * d;
+    ProfScope ps_final(m, AF_K_FINAL, s);
+    AF_K(prefinal_project(V.resid, g, d, V.mod, D.mod_cols, foff, foff + d, m->proj_out, m->dt, c.out_channels, p, h,
+                          w, out + (size_t)b0 * c.out_channels * pix, s));
     return AF_OK;
 }
 
@@ -488,12 +591,14 @@ af_status run_forward(af_model* m, const Inputs& in, int stop_after, float* resi
     const int S_pad = (S + 127) / 128 * 128;
     if (in.B == 0) return AF_OK;
 
+    // ---- per-sample prologue for the whole batch, on the caller's stream
     // key-padding bias
     {
     ProfScope ps(m, AF_K_EMBED, s);
     AF_K(key_bias(in.mask, in.T, D.R, g, S_pad, m->dt == AF_BF16 ? ATTN_BF16_KEY_KEEP : 0.f, m->kbias, s));
     }
-    // timestep embedding and every block's modulation vectors
+    // timestep embedding and every block's modulation vectors (one pass over the
+    // modulation weights for all samples)
     {
     ProfScope ps(m, AF_K_ADALN, s);
     AF_K(timestep_features(in.tau, in.B, 128, c.timestep_scale, m->tfeat, s));
@@ -501,59 +606,31 @@ af_status run_forward(af_model* m, const Inputs& in, int stop_after, float* resi
     AF_K(gemv(m->hpre, in.B, d, m->t_w2, m->dt, d, m->t_b2, 1, m->temb, s));
     AF_K(gemv(m->temb, in.B, d, m->ada, m->dt, (int)D.mod_cols, nullptr, 1, m->mod, s));
     }
-    ProfScope ps_embed(m, AF_K_EMBED, s);
-    // embeddings: image rows, register rows, caption rows
-    AF_K(patch_embed(in.latents, c.in_channels, in.H, in.W, p, m->pe_w, m->pe_b, m->dt, m->pos, D.G, m->resid, g, d, s));
-    AF_K(copy_registers(m->reg, m->dt, D.R, m->resid, g, d, s));
-    if (in.T > 0) {
-        // bf16 path: text is staged in the padded internal buffer (rounded to bf16
-        // when it arrives as fp32).
-        const void* text = in.text;
-        if (m->dt == AF_BF16) {
-            const long n = (long)in.B * in.T * c.joint_attention_dim;
-            if (in.text_dtype == AF_F32) AF_K(f32_to_bf16((const float*)in.text, m->text_bf16, n, s));
-            else AF_K(hipMemcpyAsync(m->text_bf16, in.text, (size_t)n * 2, hipMemcpyDeviceToDevice, s));
-            text = m->text_bf16;
-        }
-        GemmLaunch L = gemm_base(m, g, d, c.joint_attention_dim, EPI_STORE_MAPPED);
-        L.resid = m->resid;
-        L.seg_len = in.T;
-        L.seg_stride = g.Nt;
-        L.seg_off = D.R;
-        L.ngroups = 1;
-        L.g[0].A = text;
-        L.g[0].lda = c.joint_attention_dim;
-        L.g[0].W = m->ctx_w;
-        L.g[0].ldw = c.joint_attention_dim;
-        L.g[0].M = in.B * in.T;
-        AF_TRY(gemm(m, L, s));
+    // bf16 models stage the text in the padded internal buffer (rounded to bf16
+    // when it arrives as fp32)
+    if (in.T > 0 && m->dt == AF_BF16) {
+        ProfScope ps(m, AF_K_EMBED, s);
+        const long n = (long)in.B * in.T * c.joint_attention_dim;
+        if (in.text_dtype == AF_F32) AF_K(f32_to_bf16((const float*)in.text, m->text_bf16, n, s));
+        else AF_K(hipMemcpyAsync(m->text_bf16, in.text, (size_t)n * 2, hipMemcpyDeviceToDevice, s));
     }
-    ps_embed.end();
-    if (stop_after == -1) {
-        AF_K(taps_permute(m->resid, g, d, resid_out, s));
-        return AF_OK;
-    }
-    int bi = 0;
-    for (int j = 0; j < D.Lj; ++j, ++bi) {
-        AF_TRY(run_block(m, g, S_pad, &m->joint_txt[j], &m->joint_img[j], (long)(2 * j + 1) * 6 * d,
-                         (long)(2 * j) * 6 * d, s));
-        if (stop_after == bi) {
-            AF_K(taps_permute(m->resid, g, d, resid_out, s));
-            return AF_OK;
-        }
-    }
-    for (int i = 0; i < D.Ls; ++i, ++bi) {
-        AF_TRY(run_block(m, g, S_pad, &m->single[i], nullptr, (long)(2 * D.Lj + i) * 6 * d, 0, s));
-        if (stop_after == bi) {
-            AF_K(taps_permute(m->resid, g, d, resid_out, s));
-            return AF_OK;
-        }
-    }
-    // pre-final modulation (scale, shift) + projection + unpatchify
-    const long foff = (long)(2 * D.Lj + D.Ls) * 6 * d;
-    ProfScope ps_final(m, AF_K_FINAL, s);
-    AF_K(prefinal_project(m->resid, g, d, m->mod, D.mod_cols, foff, foff + d, m->proj_out, m->dt, c.out_channels, p, h,
-                          w, out, s));
+
+    // ---- the samples, in one or two concurrent groups. Every kernel after the
+    // prologue works on rows (or on one (sample, head)) independently, so a
+    // sample's result does not depend on the grouping.
+    if (m->groups < 2 || in.B < 2) return run_group(m, in, 0, in.B, stop_after, resid_out, out, s);
+    const int B0 = (in.B + 1) / 2;
+    AF_HIP(hipEventRecord(m->ev_fork, s));
+    AF_HIP(hipStreamWaitEvent(m->side, m->ev_fork, 0));
+    const af_status st0 = run_group(m, in, 0, B0, stop_after, resid_out, out, s);
+    const af_status st1 = run_group(m, in, B0, in.B - B0, stop_after, resid_out, out, m->side);
+    // join even after a failed launch, so the caller's stream orders after all
+    // the work that was issued
+    const hipError_t e1 = hipEventRecord(m->ev_join, m->side);
+    const hipError_t e2 = e1 == hipSuccess ? hipStreamWaitEvent(s, m->ev_join, 0) : e1;
+    if (st0 != AF_OK) return st0;
+    if (st1 != AF_OK) return st1;
+    if (e2 != hipSuccess) return fail(AF_E_HIP, std::string("join of the sample groups: ") + hipGetErrorString(e2));
     return AF_OK;
 }
 
@@ -709,6 +786,10 @@ af_status af_create(const af_config* c, int device, af_model** out) {
         *e.first = (char*)m->work + o;
         o += align256(e.second);
     }
+    if (hipStreamCreateWithFlags(&m->side, hipStreamNonBlocking) != hipSuccess ||
+        hipEventCreateWithFlags(&m->ev_fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&m->ev_join, hipEventDisableTiming) != hipSuccess)
+        return cleanup(AF_E_HIP, "stream or event creation failed");
     if (hipDeviceSynchronize() != hipSuccess) return cleanup(AF_E_HIP, "device synchronize failed");
     *out = m;
     return AF_OK;
@@ -789,6 +870,13 @@ af_status af_sigma_schedule(int num_steps, double shift, float* out) {
     return AF_OK;
 }
 
+af_status af_set_sample_groups(af_model* m, int groups) {
+    if (!m) return fail(AF_E_INVALID_ARG, "model is NULL");
+    if (groups != 1 && groups != 2) return fail(AF_E_INVALID_ARG, "groups must be 1 or 2");
+    m->groups = groups;
+    return AF_OK;
+}
+
 af_status af_profile(af_model* m, int enable) {
     if (!m) return fail(AF_E_INVALID_ARG, "model is NULL");
     DevGuard guard(m->device);
@@ -818,6 +906,10 @@ void af_destroy(af_model* m) {
             (void)hipEventDestroy(r.a);
             (void)hipEventDestroy(r.b);
         }
+        if (m->side) (void)hipStreamSynchronize(m->side);
+        if (m->ev_fork) (void)hipEventDestroy(m->ev_fork);
+        if (m->ev_join) (void)hipEventDestroy(m->ev_join);
+        if (m->side) (void)hipStreamDestroy(m->side);
         if (m->arena) (void)hipFree(m->arena);
         if (m->work) (void)hipFree(m->work);
     }
