@@ -8,10 +8,9 @@ drawn from the seeded synthetic recipe. One step = one full forward through the
 C-ABI (every kernel of the path), inputs already resident in HBM.
 
 Prints one JSON line. The timed region is bracketed by synchronisation and
-measured with HIP events on the forward's stream; with two sample groups (the
-default) the batch halves run on two concurrent streams forked from and joined
-back into that stream. The per-kernel pass (roofline, per-class times) runs the
-batch as one group so that launches do not overlap.
+measured with HIP events on the forward's stream (every kernel of the forward
+runs on it, in order). A separate per-kernel pass brackets each launch with HIP
+events on the same stream for the roofline and per-class times.
 """
 import argparse
 import json
@@ -123,8 +122,6 @@ def main():
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default="1024")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true")
-    ap.add_argument("--groups", type=int, choices=(1, 2), default=2,
-                    help="sample groups of the timed forwards (2: the batch halves run on two concurrent streams)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the forward runs on a single MI355X and this build has no "
@@ -169,7 +166,6 @@ def main():
         bad = (~torch.isfinite(out)).reshape(B, -1).sum(1).tolist()
         assert sum(bad) == 0, f"non-finite output after {where}: per-sample counts {bad}"
 
-    model.set_sample_groups(args.groups)
     for _ in range(args.warmup):
         model.forward(lat, tau, text, mask, out=out)
     torch.cuda.synchronize()
@@ -180,8 +176,6 @@ def main():
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
     def timed(n):
-        # the forward forks from and joins back into `stream`, so events on it
-        # bracket all of its work
         torch.cuda.synchronize()
         e0.record(stream)
         for _ in range(n):
@@ -197,19 +191,8 @@ def main():
     check_finite("the timed forwards")
     print(f"[bench] {ms_per_step:.2f} ms/forward, {tflops:.1f} TFLOP/s", file=sys.stderr, flush=True)
 
-    # The whole batch as one group, for comparison and for the per-kernel pass
-    # (launches of two groups overlap in time, so their durations would not be
-    # the kernels' own).
-    ms_one_group = ms_per_step
-    if args.groups != 1:
-        model.set_sample_groups(1)
-        model.forward(lat, tau, text, mask, out=out)
-        ms_one_group = timed(args.steps)
-        print(f"[bench] one group: {ms_one_group:.2f} ms/forward", file=sys.stderr, flush=True)
-
     kernels, roofline = {}, None
     if not args.no_profile:
-        model.set_sample_groups(1)
         af.af_profile(model, True)
         for _ in range(args.steps):
             model.forward(lat, tau, text, mask, out=out)
@@ -273,8 +256,6 @@ def main():
         "tflops": tflops,
         "pct_peak_bf16": 100.0 * tflops / PEAK_BF16_TFLOPS,
         "flops_per_forward": flops,
-        "sample_groups": args.groups,
-        "ms_per_step_one_group": ms_one_group,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels": kernels,

@@ -57,7 +57,6 @@ def _load():
         "af_transformer_forward_taps": (I, [P, P, P, P, I, P, I, I, I, I, I, P, P]),
         "af_flow_euler_cfg_step": (I, [P, P, I, I, I, I, F, F, F, P]),
         "af_sigma_schedule": (I, [I, D, C.POINTER(F)]),
-        "af_set_sample_groups": (I, [P, I]),
         "af_destroy": (V, [P]),
         "af_status_string": (C.c_char_p, [I]),
         "af_last_error": (C.c_char_p, []),
@@ -73,7 +72,7 @@ _lib = _load()
 EXPORTED = (
     "af_config_default", "af_check_shapes", "af_weight_count", "af_weight_info", "af_create",
     "af_load_weights", "af_init_weights", "af_transformer_forward", "af_transformer_forward_taps",
-    "af_flow_euler_cfg_step", "af_sigma_schedule", "af_set_sample_groups", "af_destroy", "af_status_string",
+    "af_flow_euler_cfg_step", "af_sigma_schedule", "af_destroy", "af_status_string",
     "af_last_error")
 
 
@@ -179,10 +178,6 @@ class AuraFlowModel:
             self.close()
         except Exception:
             pass
-
-    def set_sample_groups(self, groups: int) -> None:
-        """1: the whole batch on the call's stream; 2: two halves on concurrent streams."""
-        _check(_lib.af_set_sample_groups(self._h, int(groups)))
 
     @property
     def inner_dim(self):

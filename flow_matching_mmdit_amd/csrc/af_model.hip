@@ -167,12 +167,6 @@ struct af_model {
     size_t staging_floats = 0;
     void* work = nullptr;
 
-    // Sample groups run concurrently: group 0 on the caller's stream, group 1 on
-    // `side` (default priority, non-blocking), forked and joined with events.
-    int groups = 2;
-    hipStream_t side = nullptr;
-    hipEvent_t ev_fork = nullptr, ev_join = nullptr;
-
     // per-kernel-class event timing (af_profile)
     bool prof_on = false;
     struct Rec { hipEvent_t a, b; int cls; };
@@ -615,23 +609,8 @@ af_status run_forward(af_model* m, const Inputs& in, int stop_after, float* resi
         else AF_K(hipMemcpyAsync(m->text_bf16, in.text, (size_t)n * 2, hipMemcpyDeviceToDevice, s));
     }
 
-    // ---- the samples, in one or two concurrent groups. Every kernel after the
-    // prologue works on rows (or on one (sample, head)) independently, so a
-    // sample's result does not depend on the grouping.
-    if (m->groups < 2 || in.B < 2) return run_group(m, in, 0, in.B, stop_after, resid_out, out, s);
-    const int B0 = (in.B + 1) / 2;
-    AF_HIP(hipEventRecord(m->ev_fork, s));
-    AF_HIP(hipStreamWaitEvent(m->side, m->ev_fork, 0));
-    const af_status st0 = run_group(m, in, 0, B0, stop_after, resid_out, out, s);
-    const af_status st1 = run_group(m, in, B0, in.B - B0, stop_after, resid_out, out, m->side);
-    // join even after a failed launch, so the caller's stream orders after all
-    // the work that was issued
-    const hipError_t e1 = hipEventRecord(m->ev_join, m->side);
-    const hipError_t e2 = e1 == hipSuccess ? hipStreamWaitEvent(s, m->ev_join, 0) : e1;
-    if (st0 != AF_OK) return st0;
-    if (st1 != AF_OK) return st1;
-    if (e2 != hipSuccess) return fail(AF_E_HIP, std::string("join of the sample groups: ") + hipGetErrorString(e2));
-    return AF_OK;
+    // ---- embeddings, the blocks and the final layer for the whole batch
+    return run_group(m, in, 0, in.B, stop_after, resid_out, out, s);
 }
 
 af_status check_forward_args(af_model* m, const Inputs& in, const void* outp) {
@@ -786,10 +765,6 @@ af_status af_create(const af_config* c, int device, af_model** out) {
         *e.first = (char*)m->work + o;
         o += align256(e.second);
     }
-    if (hipStreamCreateWithFlags(&m->side, hipStreamNonBlocking) != hipSuccess ||
-        hipEventCreateWithFlags(&m->ev_fork, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&m->ev_join, hipEventDisableTiming) != hipSuccess)
-        return cleanup(AF_E_HIP, "stream or event creation failed");
     if (hipDeviceSynchronize() != hipSuccess) return cleanup(AF_E_HIP, "device synchronize failed");
     *out = m;
     return AF_OK;
@@ -870,13 +845,6 @@ af_status af_sigma_schedule(int num_steps, double shift, float* out) {
     return AF_OK;
 }
 
-af_status af_set_sample_groups(af_model* m, int groups) {
-    if (!m) return fail(AF_E_INVALID_ARG, "model is NULL");
-    if (groups != 1 && groups != 2) return fail(AF_E_INVALID_ARG, "groups must be 1 or 2");
-    m->groups = groups;
-    return AF_OK;
-}
-
 af_status af_profile(af_model* m, int enable) {
     if (!m) return fail(AF_E_INVALID_ARG, "model is NULL");
     DevGuard guard(m->device);
@@ -906,10 +874,6 @@ void af_destroy(af_model* m) {
             (void)hipEventDestroy(r.a);
             (void)hipEventDestroy(r.b);
         }
-        if (m->side) (void)hipStreamSynchronize(m->side);
-        if (m->ev_fork) (void)hipEventDestroy(m->ev_fork);
-        if (m->ev_join) (void)hipEventDestroy(m->ev_join);
-        if (m->side) (void)hipStreamDestroy(m->side);
         if (m->arena) (void)hipFree(m->arena);
         if (m->work) (void)hipFree(m->work);
     }

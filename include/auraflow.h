@@ -147,11 +147,8 @@ af_status af_init_weights(af_model* m, const float* host_blob, size_t n_floats, 
  *               Padding keys are excluded from every attention; register and
  *               image keys are always valid.
  *   out         device fp32 [B, out_channels, H, W]
- * The workspace is reused; nothing is allocated. With two sample groups (the
- * default, see af_set_sample_groups) and B >= 2, the work after the per-sample
- * prologue runs as two independent halves of the batch, the first on `stream`
- * and the second on a stream the model owns, forked from and joined back into
- * `stream` with events: the call stays ordered on `stream` as one unit.
+ * The workspace is reused; nothing is allocated. Every kernel of the call is
+ * launched on `stream`, in order.
  */
 af_status af_transformer_forward(af_model* m, const float* latents, const float* timestep,
                                  const void* text_embeds, af_dtype text_dtype,
@@ -193,22 +190,9 @@ af_status af_flow_euler_cfg_step(float* latents, const float* v, int Bi, int C, 
 af_status af_sigma_schedule(int num_steps, double shift, float* sigmas_out);
 
 /*
- * Execution option (not a method step): the number of groups the batch is split
- * into after the per-sample prologue (key bias, timestep and modulation
- * vectors, text staging). groups = 2 runs samples [0, ceil(B/2)) and the rest
- * concurrently on two streams, so the wave-quantisation tail of one group's
- * kernel is filled by the other group's work; groups = 1 runs the whole batch
- * on `stream`. Every kernel after the prologue treats rows (and attention each
- * (sample, head)) independently, so the outputs are bit-identical either way.
- * Default 2. Errors: AF_E_INVALID_ARG for a NULL model or groups not 1 or 2.
- */
-af_status af_set_sample_groups(af_model* m, int groups);
-
-/*
  * Diagnostics: per-kernel-class timing. While enabled, every kernel launch of
  * af_transformer_forward / _taps is bracketed by a pair of hipEvents recorded
- * on the stream it is launched on (with two sample groups the classes then sum
- * the launches of both groups, which overlap in time). af_profile(m, 1) clears the counters and starts;
+ * on the call's stream. af_profile(m, 1) clears the counters and starts;
  * af_profile(m, 0) stops. af_profile_read waits for the recorded events and
  * returns, for one class, the summed kernel time in milliseconds and the
  * number of launches since the last af_profile(m, 1).

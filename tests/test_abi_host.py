@@ -143,9 +143,3 @@ def test_forward_rejects_null_model(af):
     st = lib.af_transformer_forward(None, None, None, None, 0, None, 1, 16, 16, 8, None, None)
     assert st == af.AF_E_INVALID_ARG
     assert b"model" in lib.af_last_error()
-
-
-def test_set_sample_groups_rejects_null_model(af):
-    # host-only validation: no device is touched for a NULL handle
-    assert af._lib.af_set_sample_groups(None, 2) == af.AF_E_INVALID_ARG
-    assert "NULL" in af._lib.af_last_error().decode()

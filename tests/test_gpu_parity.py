@@ -178,44 +178,6 @@ def test_small_bf16_deterministic_and_mask_invariant(af, small_bf16):
     np.testing.assert_array_equal(d1, d2)
 
 
-def test_small_bf16_sample_groups_bit_identical(af, small_bf16):
-    """B = 3 split as [2, 1] over two streams against the whole batch on one
-    stream: outputs and every residual tap are bit-identical, and an invalid
-    group count is rejected on the host."""
-    torch = _torch()
-    cfg, m, dev, ref, taps, _ = small_bf16
-    try:
-        m.set_sample_groups(2)
-        two = [m.forward_taps(*dev, stop_after_block=blk).cpu().numpy() for blk in (-1, 0, 2)]
-        two.append(m.forward(*dev).cpu().numpy())
-        m.set_sample_groups(1)
-        one = [m.forward_taps(*dev, stop_after_block=blk).cpu().numpy() for blk in (-1, 0, 2)]
-        one.append(m.forward(*dev).cpu().numpy())
-        torch.cuda.synchronize()
-        for a, b in zip(two, one):
-            np.testing.assert_array_equal(a, b)
-        with pytest.raises(ValueError):
-            m.set_sample_groups(3)
-    finally:
-        m.set_sample_groups(2)
-
-
-def test_tiny_fp32_sample_groups_bit_identical(af, tiny):
-    torch = _torch()
-    cfg, m = tiny
-    lat, taus, text, mask = workload_inputs(2, 4, 12, 16, 8, 32, lengths=[8, 3], cfg_pairs=False)
-    dev = (to_dev(lat), to_dev(taus), to_dev(text), to_dev(mask))
-    try:
-        m.set_sample_groups(2)
-        a = m.forward(*dev).cpu().numpy()
-        m.set_sample_groups(1)
-        b = m.forward(*dev).cpu().numpy()
-        torch.cuda.synchronize()
-        np.testing.assert_array_equal(a, b)
-    finally:
-        m.set_sample_groups(2)
-
-
 def test_small_bf16_bf16_text_input(af, small_bf16):
     torch = _torch()
     cfg, m, dev, ref, taps, host = small_bf16
