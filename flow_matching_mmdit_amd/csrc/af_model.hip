@@ -163,6 +163,8 @@ struct af_model {
     float* raw = nullptr;  // fp32 path only
     float *mod = nullptr, *temb = nullptr, *hpre = nullptr, *tfeat = nullptr, *kbias = nullptr;
     bf16_t* text_bf16 = nullptr;
+    float* attn_part = nullptr;  // partial sums of split attention query tiles (bf16 path)
+    int n_cu = 0;                // compute units of the device
     float* staging = nullptr;
     size_t staging_floats = 0;
     void* work = nullptr;
@@ -465,7 +467,7 @@ af_status run_block(af_model* m, const View& V, RowGeom g, int S_pad, const Bloc
     ProfScope ps(m, AF_K_ATTENTION, s);
     if (m->dt == AF_BF16)
         AF_K(attention_bf16((const bf16_t*)V.q, (const bf16_t*)V.k, (const bf16_t*)V.v, V.kbias, g, D.H, S_pad,
-                            (bf16_t*)V.attn, d, s));
+                            (bf16_t*)V.attn, d, m->n_cu, m->attn_part, s));
     else
         AF_K(attention_f32((const float*)V.q, (const float*)V.k, (const float*)V.v, V.kbias, g, D.H, D.hd, S_pad,
                            (float*)V.attn, d, s));
@@ -753,6 +755,9 @@ af_status af_create(const af_config* c, int device, af_model** out) {
         {(void**)&m->text_bf16, (size_t)Tp * c->joint_attention_dim * 2},
     };
     if (m->dt == AF_F32) ws.push_back({(void**)&m->raw, Mm * std::max(3 * d, 2 * F) * 4});
+    if (hipDeviceGetAttribute(&m->n_cu, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || m->n_cu <= 0)
+        return cleanup(AF_E_HIP, "compute-unit count query failed");
+    if (m->dt == AF_BF16) ws.push_back({(void**)&m->attn_part, attention_bf16_part_floats(m->n_cu) * 4});
     m->staging_floats = 16u << 20;
     ws.push_back({(void**)&m->staging, m->staging_floats * 4});
     size_t wtotal = 0;

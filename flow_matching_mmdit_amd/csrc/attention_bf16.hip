@@ -62,7 +62,8 @@ __device__ __forceinline__ int vswz(int row) { return (row & 7) ^ ((row >> 3) & 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_attention_bf16(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
                       const bf16_t* __restrict__ Vt, const float* __restrict__ bias, RowGeom g, int H,
-                      int S_pad, bf16_t* __restrict__ O, int d) {
+                      int S_pad, bf16_t* __restrict__ O, int d, int nqt, int nfull, int kp,
+                      float* __restrict__ part) {
     // K slot 0, K slot 1, v^T slot 0, v^T slot 1, then per slot and wave a 1 KB
     // bias block (4 copies of 64 fp32 keys)
     __shared__ __attribute__((aligned(1024))) bf16_t smem[4 * KTILE + 2 * 4 * 512];
@@ -71,9 +72,32 @@ void k_attention_bf16(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K
     // is then formed with scalar arithmetic
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int grp = lane >> 5, l32 = lane & 31;
-    const int b = blockIdx.z, h = blockIdx.y;
     const int S = g.S();
-    const int q0 = blockIdx.x * QT + wave * 32;
+    const int ntiles = (S + KT - 1) / KT;
+    // Work item -> (sample b, head h, query tile qt) and key-tile range [kt0, kt1).
+    // Items [0, nfull) are whole query tiles, in (b, h, qt) order with qt fastest,
+    // spread so that the items of one XCD (block ids are dispatched round-robin
+    // over the 8 XCDs) are consecutive and share K and v^T in that XCD's L2.
+    // Items past nfull are pieces: each remaining query tile is split into kp
+    // key ranges whose partial sums are added by k_attention_combine.
+    int tq, piece = -1, kt0 = 0, kt1 = ntiles;
+    {
+        const int bid = blockIdx.x;
+        if (bid < nfull) {
+            const int x = bid % 8, qq = nfull / 8, rr = nfull % 8;
+            tq = x * qq + min(x, rr) + bid / 8;
+        } else {
+            const int j = bid - nfull;
+            tq = nfull + j / kp;
+            piece = j;
+            const int pi = j % kp;
+            kt0 = ntiles * pi / kp;
+            kt1 = ntiles * (pi + 1) / kp;
+        }
+    }
+    const int qt = tq % nqt, h = (tq / nqt) % H, b = tq / (nqt * H);
+    const int nt = kt1 - kt0;   // key tiles of this item
+    const int q0 = qt * QT + wave * 32;
     const long bh = (long)b * H + h;
     const bf16_t* Kbh = K + bh * S_pad * HD;
     const bf16_t* Vbh = Vt + bh * HD * (long)S_pad;
@@ -103,21 +127,21 @@ void k_attention_bf16(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K
     const __amdgpu_buffer_rsrc_t rK = __builtin_amdgcn_make_buffer_rsrc((void*)Kbh, (short)0, S_pad * HD * 2, 0x00020000);
     const __amdgpu_buffer_rsrc_t rV = __builtin_amdgcn_make_buffer_rsrc((void*)Vbh, (short)0, S_pad * HD * 2, 0x00020000);
     const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc((void*)biasb, (short)0, S_pad * 4, 0x00020000);
-    const int ntiles = (S + KT - 1) / KT;
-    // one direct load of tile `tile` (clamped to the last tile: the loads issued
-    // past the end re-read it into a slot nobody reads again)
+    // one direct load of the item's key tile `tile` (relative to kt0; clamped to
+    // its last tile: the loads issued past the end re-read it into a slot nobody
+    // reads again)
     auto issue_k = [&](int j, int tile, int slot) {
-        const int k0 = min(tile, ntiles - 1) * KT;
+        const int k0 = (kt0 + min(tile, nt - 1)) * KT;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rK, (lds_void*)(kslot(slot) + (wave * 8 + j) * 512), 16, koff[j],
                                                  k0 * HD * 2, 0, 0);
     };
     auto issue_v = [&](int j, int tile, int slot) {
-        const int k0 = min(tile, ntiles - 1) * KT;
+        const int k0 = (kt0 + min(tile, nt - 1)) * KT;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rV, (lds_void*)(vslot(slot) + (wave * 8 + j) * 512), 16, voff[j & 1],
                                                  k0 * 2 + (j & ~1) * 8 * S_pad * 2, 0, 0);
     };
     auto issue_b = [&](int tile, int slot) {
-        const int k0 = min(tile, ntiles - 1) * KT;
+        const int k0 = (kt0 + min(tile, nt - 1)) * KT;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_void*)(smem + 4 * KTILE + (slot * 4 + wave) * 512), 16,
                                                  (lane & 15) * 16, k0 * 4, 0, 0);
     };
@@ -129,7 +153,7 @@ void k_attention_bf16(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K
     bf16x8 qf[16];
     {
         bf16_t* sQ = vslot(0);                         // 64 KB: rows of 512 B
-        const bf16_t* qsrc = Q + (bh * S_pad + (long)blockIdx.x * QT) * HD;
+        const bf16_t* qsrc = Q + (bh * S_pad + (long)qt * QT) * HD;
         const __amdgpu_buffer_rsrc_t rQ = __builtin_amdgcn_make_buffer_rsrc((void*)qsrc, (short)0, QT * HD * 2, 0x00020000);
         // 128 rows x 32 chunks = 64 instructions of 1 KB, 16 per wave; lane -> row
         // 2 cb + (lane >> 5), physical chunk lane & 31, logical chunk pc ^ (row & 31).
@@ -285,15 +309,29 @@ void k_attention_bf16(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K
         l_run += psum;
     };
     int t = 0;
-    for (; t + 1 < ntiles; t += 2) {
+    for (; t + 1 < nt; t += 2) {
         iteration(t, sa, sb);
         iteration(t + 1, sb, sa);
     }
-    if (t < ntiles) iteration(t, sa, sb);
+    if (t < nt) iteration(t, sa, sb);
     __builtin_amdgcn_s_waitcnt(0);
 
-    // ---- normalise and store: lane has query q0 + (lane & 31), head dims ht*32 + i*8 + 4 (lane>>5) + j
+    // lane has query q0 + (lane & 31), head dims ht*32 + i*8 + 4 (lane>>5) + j
     const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    if (piece >= 0) {
+        // a piece: unnormalised partial O and its sum of p, fp32
+        float* blk = part + (size_t)piece * (QT * HD + QT);
+        const int ql = wave * 32 + l32;
+#pragma unroll
+        for (int ht = 0; ht < 8; ++ht)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                *reinterpret_cast<float4*>(blk + ql * HD + ht * 32 + i * 8 + grp * 4) =
+                    make_float4(o[ht][i * 4 + 0], o[ht][i * 4 + 1], o[ht][i * 4 + 2], o[ht][i * 4 + 3]);
+        if (grp == 0) blk[QT * HD + ql] = l_tot;
+        return;
+    }
+    // ---- normalise and store
     const float inv = 1.f / l_tot;
     const int q = q0 + l32;
     if (q < S) {
@@ -309,12 +347,56 @@ void k_attention_bf16(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K
     }
 }
 
+// Sum of the kp partial results of each split query tile, normalised, to O.
+// One wave per query: lane l holds head dims [4 l, 4 l + 4).
+__global__ __launch_bounds__(256) void k_attention_combine(const float* __restrict__ part, int nfull, int kp,
+                                                           int ntail, int nqt, int H, RowGeom g,
+                                                           bf16_t* __restrict__ O, int d) {
+    const int lane = threadIdx.x & 63;
+    const int w = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+    if (w >= ntail * QT) return;
+    const int j = w / QT, ql = w % QT;
+    const int tq = nfull + j;
+    const int qt = tq % nqt, h = (tq / nqt) % H, b = tq / (nqt * H);
+    const int q = qt * QT + ql;
+    if (q >= g.S()) return;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    float l = 0.f;
+    for (int p = 0; p < kp; ++p) {
+        const float* blk = part + (size_t)(j * kp + p) * (QT * HD + QT);
+        const float4 v = *reinterpret_cast<const float4*>(blk + ql * HD + lane * 4);
+        acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+        l += blk[QT * HD + ql];
+    }
+    const float inv = 1.f / l;
+    *reinterpret_cast<uint2*>(O + (long)g.row_of(b, q) * d + h * HD + lane * 4) =
+        make_uint2(pack2bf(acc.x * inv, acc.y * inv), pack2bf(acc.z * inv, acc.w * inv));
+}
+
+size_t attention_bf16_part_floats(int n_cu) { return (size_t)n_cu * (QT * HD + QT); }
+
 hipError_t attention_bf16(const bf16_t* q, const bf16_t* k, const bf16_t* vt, const float* bias, RowGeom g, int H,
-                          int S_pad, bf16_t* o, int d, hipStream_t s) {
-    int S = g.S();
+                          int S_pad, bf16_t* o, int d, int n_cu, float* part, hipStream_t s) {
+    const int S = g.S();
     if (g.B == 0 || S == 0) return hipSuccess;
-    dim3 grid((S + QT - 1) / QT, H, g.B);
-    hipLaunchKernelGGL(k_attention_bf16, grid, dim3(256), 0, s, q, k, vt, bias, g, H, S_pad, o, d);
+    const int nqt = (S + QT - 1) / QT, ntiles = (S + KT - 1) / KT;
+    const int total = nqt * H * g.B;
+    // Wave quantisation: the last `total % n_cu` query tiles would run as a
+    // partial round on the n_cu compute units (one workgroup per CU). They are
+    // split into kp key ranges each (kp * tail <= n_cu, at least two key tiles
+    // per piece) so the partial round is kp times shorter.
+    int tail = part && n_cu > 0 ? total % n_cu : 0;
+    int kp = tail ? min(n_cu / tail, ntiles / 2) : 1;
+    if (kp < 2) tail = 0, kp = 1;
+    const int nfull = total - tail;
+    hipLaunchKernelGGL(k_attention_bf16, dim3(nfull + tail * kp), dim3(256), 0, s, q, k, vt, bias, g, H, S_pad, o, d,
+                       nqt, nfull, kp, part);
+    if (tail) {
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(k_attention_combine, dim3((tail * QT * 64 + 255) / 256), dim3(256), 0, s, part, nfull, kp,
+                           tail, nqt, H, g, o, d);
+    }
     return hipGetLastError();
 }
 

@@ -6,7 +6,7 @@ batch 2, and the 25-step sampling loop with 4 images (transformer batch 8).
 Oracle comparisons use the float32 oracle with the same bf16-rounded weights and
 text; the bar is max|d|/max|ref| <= 2e-2 and cosine >= 0.999 per block output.
 Where the oracle cannot follow (25 steps at batch 8), properties that hold at
-any size are checked bit for bit.
+any size are checked (bit for bit where the launch configuration is the same).
 """
 import numpy as np
 import pytest
@@ -100,8 +100,11 @@ def test_full_1536_first_joint_block(af, full):
 
 def test_full_sampling_loop_batch_composition(af, full):
     """25-step CFG sampling of 4 images (transformer batch 8): every image's
-    trajectory is bit-identical to sampling it alone, and the loop equals the
-    explicit forward + Euler-CFG composition."""
+    trajectory matches sampling it alone (to the bf16 bar: the attention splits
+    the work of the last partial round of query tiles over key ranges, and
+    which tiles are split depends on the batch size, so the fp32 summation
+    order of those tiles differs), and the loop equals the explicit forward +
+    Euler-CFG composition bit for bit."""
     import torch
     cfg, m = full
     Bp, T = 4, 256
@@ -121,7 +124,10 @@ def test_full_sampling_loop_batch_composition(af, full):
     ti = np.concatenate([text_u[i:i + 1], text_c[i:i + 1]])
     mi = np.concatenate([mask[i:i + 1], mask[Bp + i:Bp + i + 1]])
     m.sample(xi, to_dev(ti), to_dev(mi), num_steps=25, shift=1.73, guidance=3.5)
-    np.testing.assert_array_equal(xi.cpu().numpy()[0], xb[i])
+    alone = xi.cpu().numpy()[0]
+    e, c = rel_max(alone, xb[i]), cosine(alone, xb[i])
+    print(f"image {i} alone vs in batch 8 after 25 steps: rel {e:.3e} cos {c:.6f}")
+    assert e <= TOL and c >= COS, (e, c)
     # The loop's step is the explicit forward + Euler-CFG composition (one step).
     sig1 = af.af_sigma_schedule(1, 1.73)
     xin = to_dev(np.concatenate([x0, x0]))
