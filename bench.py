@@ -71,6 +71,49 @@ def class_work(name, d, F, B, S):
     return None, None
 
 
+# HBM traffic per launch of a kernel class, from rocprofv3 FETCH_SIZE / WRITE_SIZE
+# counter runs summarised under profiles/. A summary names the kernel's source
+# files and the sha256 of their concatenation; when a source has changed since,
+# the figure no longer describes the kernel and is not reported.
+TRAFFIC_PROFILES = {
+    "gemm_ffn_up": "profiles/gemm_ffn_up_1024x1024_cfg2_hbm_traffic.md",
+}
+
+
+def measured_traffic(kclass):
+    import hashlib
+    path = TRAFFIC_PROFILES.get(kclass)
+    if path is None or not os.path.exists(os.path.join(ROOT, path)):
+        return None
+    fields = {}
+    for line in open(os.path.join(ROOT, path)):
+        if ":" in line and line.startswith("- `"):
+            k, v = line[3:].split("`", 1)[0], line.split(":", 1)[1].strip().strip("`")
+            fields[k] = v
+    srcs = fields.get("kernel_source", "").split()
+    if not srcs or not all(os.path.exists(os.path.join(ROOT, f)) for f in srcs):
+        return None
+    h = hashlib.sha256()
+    for f in srcs:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    digest = h.hexdigest()
+    if digest != fields.get("source_sha256"):
+        return None
+    return float(fields["hbm_bytes_per_launch"])
+
+
+def copy_calibration():
+    """A plain device copy of 512 MiB, four times: the reference the FETCH_SIZE and
+    WRITE_SIZE counters are scaled by (run under rocprofv3 --pmc)."""
+    import torch
+    a = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(4):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(f"copied {a.numel() * 4} bytes, 4 times", flush=True)
+
+
 def cpu_baseline(workload, threads):
     """The oracle (fp32 numpy) on a bounded sample: embedding + one joint block +
     one single block at the full workload shape; forward time extrapolated as
@@ -122,11 +165,17 @@ def main():
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default="1024")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run the plain 512 MiB device copy used to scale the HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the forward runs on a single MI355X and this build has no "
               f"multi-GPU path (--gpus {args.gpus} requested).", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     import torch
     import flow_matching_mmdit_amd as pkg
@@ -223,11 +272,11 @@ def main():
             if kind == "mfma":
                 roofline = {"bound": "mfma", "kernel": name, "achieved": work / avg / 1e12,
                             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                            "frac": work / avg / 1e12 / PEAK_BF16_TFLOPS, "traffic": None,
+                            "frac": work / avg / 1e12 / PEAK_BF16_TFLOPS, "traffic": measured_traffic(name),
                             "avg_launch_ms": avg * 1e3, "work_per_launch": work}
             else:
                 roofline = {"bound": "hbm", "kernel": name, "achieved": work / avg / 1e9, "peak": PEAK_HBM_GBS,
-                            "unit": "GB/s", "frac": work / avg / 1e9 / PEAK_HBM_GBS, "traffic": None,
+                            "unit": "GB/s", "frac": work / avg / 1e9 / PEAK_HBM_GBS, "traffic": measured_traffic(name),
                             "avg_launch_ms": avg * 1e3, "work_per_launch": work}
 
     cpu = None

@@ -39,7 +39,7 @@ def _taps_ref(ocfg, W, lat, tau, text, mask, dtype):
 def _tiny_cfg(af, **kw):
     base = dict(compute_dtype=af.AF_F32, num_attention_heads=4, attention_head_dim=8, caption_projection_dim=32,
                 joint_attention_dim=32, pos_embed_max_size=64, num_mmdit_layers=1, num_single_dit_layers=1,
-                max_batch=2, max_latent_h=16, max_latent_w=16, max_text_len=8)
+                max_batch=6, max_latent_h=16, max_latent_w=16, max_text_len=8)
     base.update(kw)
     return af.make_config(**base)
 
@@ -58,6 +58,7 @@ def tiny(af):
     (2, 12, 16, 8, [8, 3], None),              # ragged: 6 x 8 patch grid, off-centre crop, padding masked
     (2, 16, 10, 5, [5, 1], None),              # non-square, short text
     (1, 4, 4, 0, None, 0.25),                  # no text tokens at all
+    (6, 12, 14, 6, [6, 2, 5, 1, 3, 4], None),  # more samples than the patch embedding stages at once
 ])
 def test_tiny_fp32_forward_matches_oracle(af, tiny, B, H, W, T, lengths, tau):
     torch = _torch()
