@@ -114,7 +114,7 @@ def copy_calibration():
     print(f"copied {a.numel() * 4} bytes, 4 times", flush=True)
 
 
-def cpu_baseline(workload, threads):
+def cpu_baseline(shape, threads):
     """The oracle (fp32 numpy) on a bounded sample: embedding + one joint block +
     one single block at the full workload shape; forward time extrapolated as
     embed + 4 joint + 32 single."""
@@ -122,7 +122,7 @@ def cpu_baseline(workload, threads):
     import seeded_inputs
     from oracle import transformer as T_
 
-    B, H, W, T = WORKLOADS[workload]
+    B, H, W, T = shape
     cfg = oracle.FULL
     lat = np.concatenate([seeded_inputs.latents(1, 4, H, W)] * B)
     tau = np.full(B, 0.5, np.float32)
@@ -151,7 +151,7 @@ def cpu_baseline(workload, threads):
     return {
         "value": 1.0 / t_fwd, "unit": "forwards/s", "cores": threads, "kind": "oracle",
         "sample": (f"numpy fp32 oracle, BLAS threads={threads}: embedding ({t_embed:.2f} s) + 1 joint block "
-                   f"({t_joint:.2f} s) + 1 single block ({t_single:.2f} s) at the full {workload}^2 CFG-batch-2 "
+                   f"({t_joint:.2f} s) + 1 single block ({t_single:.2f} s) at the full {8 * W}x{8 * H}-pixel CFG-batch-2 "
                    f"shape; forward extrapolated as embed + 4 joint + 32 single = {t_fwd:.1f} s; weight "
                    f"generation ({gen_s:.1f} s) excluded"),
     }
@@ -163,6 +163,8 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default="1024")
+    ap.add_argument("--latent", default=None, metavar="HxW",
+                    help="any latent size (even, at most 192 x 192) instead of the workload's square one")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -188,6 +190,8 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     B, H, W, T = WORKLOADS[args.workload]
+    if args.latent:
+        H, W = (int(x) for x in args.latent.lower().split("x"))
     cfg = af.make_config(max_batch=B, max_latent_h=H, max_latent_w=W, max_text_len=T)
     d = cfg.num_attention_heads * cfg.attention_head_dim
     F = ((8 * d) // 3 + 255) // 256 * 256
@@ -282,7 +286,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         print(f"[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(args.workload, _cpu_threads())
+        cpu = cpu_baseline((B, H, W, T), _cpu_threads())
 
     res = {
         "metric": "AuraFlow transformer forwards/s at 1024² CFG batch 2; TFLOP/s as % of bf16 peak",
@@ -297,7 +301,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"AuraFlow transformer forward at {args.workload}x{args.workload} "
+        "config": {"workload": f"AuraFlow transformer forward at {8 * W}x{8 * H} pixels "
                                f"(latent 4x{H}x{W}: {Nimg} image + 8 register + {T} text tokens), CFG batch {B}, "
                                f"4 joint + 32 single blocks, d=3072, 12x256 heads, FFN 8192, seeded random "
                                f"bf16 weights (6.86B params), padded text masked",

@@ -98,6 +98,32 @@ def test_full_1536_first_joint_block(af, full):
     assert e <= TOL and c >= COS, (e, c)
 
 
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("H,W", [(126, 94), (66, 158), (150, 40)])
+def test_full_any_resolution_first_joint_block(af, full, H, W):
+    """One library instance (workspace sized for 192 x 192 latents) serving
+    non-square resolutions whose patch grids leave odd margins in the 96 x 96
+    position table (centre crop offsets rounded down): the residual after the
+    first joint block matches the oracle, and the whole forward is finite."""
+    import torch
+    cfg, m = full
+    ocfg = oracle_cfg(cfg)
+    lat, taus, text, mask = _inputs(H, W)
+    dev = (to_dev(lat), to_dev(taus), to_dev(text), to_dev(mask))
+    got0 = m.forward_taps(*dev, stop_after_block=0).cpu().numpy()
+    out = m.forward(*dev).cpu().numpy()
+    torch.cuda.synchronize()
+    assert np.isfinite(out).all() and out.shape == (2, 4, H, W)
+    W_o = PrefetchWeights(ocfg).as_weights()
+    temb, xt, xi, kv = oracle.embed(ocfg, W_o, lat, taus, text, mask, np.float32)
+    blk = lambda p: {k: W_o[p + k] for k in ("ada", "wq", "wk", "wv", "wo", "ff1", "ff2", "ff3")}
+    xt, xi = oracle.joint_block(ocfg, blk("joint0.img."), blk("joint0.txt."), temb, xt, xi, kv, np.float32)
+    ref0 = np.concatenate([xt, xi], 1)
+    e, c = rel_max(got0, ref0), cosine(got0, ref0)
+    print(f"{H}x{W} block 0: rel {e:.3e} cos {c:.6f}")
+    assert e <= TOL and c >= COS, (H, W, e, c)
+
+
 def test_full_sampling_loop_batch_composition(af, full):
     """25-step CFG sampling of 4 images (transformer batch 8): every image's
     trajectory matches sampling it alone (to the bf16 bar: the attention splits
