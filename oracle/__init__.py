@@ -24,16 +24,16 @@ design notes) is not established; each reading is a self-consistent definition.
 """
 from .spec import (AuraFlowConfig, find_multiple, weight_specs, count_parameters,
                    TINY, BLOCK_PAIR, FULL)
-from .numerics import round_bf16
+from .numerics import round_bf16, round_e4m3, mxfp8_qdq
 from .transformer import (layer_norm, modulate, timestep_embedding, timestep_mlp,
                           pe_crop_indices, patchify, unpatchify, patch_embed,
                           attention, feed_forward, joint_block, single_block,
-                          pre_final, embed, forward, Weights)
+                          pre_final, embed, forward, Weights, mx_block)
 from .sampling import sigma_schedule, cfg_combine, euler_step, cfg_euler_step
 
 __all__ = [
     "AuraFlowConfig", "find_multiple", "weight_specs", "count_parameters",
-    "TINY", "BLOCK_PAIR", "FULL", "round_bf16",
+    "TINY", "BLOCK_PAIR", "FULL", "round_bf16", "round_e4m3", "mxfp8_qdq", "mx_block",
     "layer_norm", "modulate", "timestep_embedding", "timestep_mlp", "pe_crop_indices",
     "patchify", "unpatchify", "patch_embed", "attention", "feed_forward", "joint_block",
     "single_block", "pre_final", "embed", "forward", "Weights",

@@ -14,7 +14,7 @@ from __future__ import annotations
 import numpy as np
 
 import seeded_inputs
-from .numerics import round_bf16
+from .numerics import round_bf16, mxfp8_qdq
 from .spec import AuraFlowConfig, weight_specs
 
 
@@ -181,15 +181,34 @@ def attention(q, k, v, key_valid, scale):
     return out
 
 
-def feed_forward(n, w1, w2, w3):
-    """SiLU-gated FFN: (silu(n W1^T) * (n W2^T)) W3^T ([PIPE] 深入源码 (前馈网络))."""
-    return (silu(n @ w1.T) * (n @ w2.T)) @ w3.T
+def feed_forward(n, w1, w2, w3, mx=False):
+    """SiLU-gated FFN: (silu(n W1^T) * (n W2^T)) W3^T ([PIPE] 深入源码 (前馈网络)).
+    mx: the hidden activations are MXFP8-quantized before W3 (operands n and the
+    weights arrive already quantized)."""
+    return _mxq(silu(n @ w1.T) * (n @ w2.T), mx) @ w3.T
 
 
 def _mod6(temb, ada):
     """Six modulation vectors [shift1, scale1, gate1, shift2, scale2, gate2] from SiLU(temb) A^T."""
     m = silu(temb) @ ada.T
     return np.split(m, 6, axis=1)
+
+
+# MXFP8 block GEMMs (mx=True): the QKV projection and both FFN products take
+# MXFP8 operands -- the LayerNorm + modulate output, the SiLU-gated hidden
+# activations and the weights of those three products are quantized along their
+# contraction axis (mxfp8_qdq) and the products accumulate in the working
+# precision. The out-projection, attention and everything else are unchanged.
+MX_WEIGHTS = ("wq", "wk", "wv", "ff1", "ff2", "ff3")
+
+
+def mx_block(blk):
+    """A block's weight dict with the MXFP8 GEMM weights quantized and dequantized."""
+    return {k: (mxfp8_qdq(v) if k in MX_WEIGHTS else v) for k, v in blk.items()}
+
+
+def _mxq(x, mx):
+    return mxfp8_qdq(x).astype(x.dtype) if mx else x
 
 
 def _qkv(n, blk, cfg, dtype):
@@ -201,7 +220,7 @@ def _qkv(n, blk, cfg, dtype):
     return q, k, v
 
 
-def joint_block(cfg, blk_img, blk_txt, temb, x_txt, x_img, key_valid, dtype=np.float32):
+def joint_block(cfg, blk_img, blk_txt, temb, x_txt, x_img, key_valid, dtype=np.float32, mx=False):
     """One MMDiT block: two streams with their own weights sharing one attention.
 
     [TRANS] 核心子模块架构 (联合注意力块) and 注意力处理器与 QKV 融合: per stream
@@ -211,10 +230,12 @@ def joint_block(cfg, blk_img, blk_txt, temb, x_txt, x_img, key_valid, dtype=np.f
     eps = dtype(cfg.ln_eps)
     scale = dtype(1.0 / np.sqrt(cfg.attention_head_dim))
     Nt = x_txt.shape[1]
+    if mx:
+        blk_img, blk_txt = mx_block(blk_img), mx_block(blk_txt)
     mi = _mod6(temb, blk_img["ada"])
     mt = _mod6(temb, blk_txt["ada"])
-    n_img = modulate(layer_norm(x_img, eps), mi[0], mi[1])
-    n_txt = modulate(layer_norm(x_txt, eps), mt[0], mt[1])
+    n_img = _mxq(modulate(layer_norm(x_img, eps), mi[0], mi[1]), mx)
+    n_txt = _mxq(modulate(layer_norm(x_txt, eps), mt[0], mt[1]), mx)
     qi, ki, vi = _qkv(n_img, blk_img, cfg, dtype)
     qt, kt, vt = _qkv(n_txt, blk_txt, cfg, dtype)
     o = attention(np.concatenate([qt, qi], axis=2), np.concatenate([kt, ki], axis=2),
@@ -223,14 +244,14 @@ def joint_block(cfg, blk_img, blk_txt, temb, x_txt, x_img, key_valid, dtype=np.f
     o_txt, o_img = o[:, :Nt], o[:, Nt:]
     x_img = x_img + mi[2][:, None, :] * (o_img @ blk_img["wo"].T)
     x_txt = x_txt + mt[2][:, None, :] * (o_txt @ blk_txt["wo"].T)
-    n_img = modulate(layer_norm(x_img, eps), mi[3], mi[4])
-    n_txt = modulate(layer_norm(x_txt, eps), mt[3], mt[4])
-    x_img = x_img + mi[5][:, None, :] * feed_forward(n_img, blk_img["ff1"], blk_img["ff2"], blk_img["ff3"])
-    x_txt = x_txt + mt[5][:, None, :] * feed_forward(n_txt, blk_txt["ff1"], blk_txt["ff2"], blk_txt["ff3"])
+    n_img = _mxq(modulate(layer_norm(x_img, eps), mi[3], mi[4]), mx)
+    n_txt = _mxq(modulate(layer_norm(x_txt, eps), mt[3], mt[4]), mx)
+    x_img = x_img + mi[5][:, None, :] * feed_forward(n_img, blk_img["ff1"], blk_img["ff2"], blk_img["ff3"], mx)
+    x_txt = x_txt + mt[5][:, None, :] * feed_forward(n_txt, blk_txt["ff1"], blk_txt["ff2"], blk_txt["ff3"], mx)
     return x_txt, x_img
 
 
-def single_block(cfg, blk, temb, x, key_valid, dtype=np.float32):
+def single_block(cfg, blk, temb, x, key_valid, dtype=np.float32, mx=False):
     """One DiT block over the concatenated [registers; text; image] sequence.
 
     [TRANS] 核心子模块架构 (单 DiT 块): self-attention over one sequence with the
@@ -238,13 +259,15 @@ def single_block(cfg, blk, temb, x, key_valid, dtype=np.float32):
     """
     eps = dtype(cfg.ln_eps)
     scale = dtype(1.0 / np.sqrt(cfg.attention_head_dim))
+    if mx:
+        blk = mx_block(blk)
     m = _mod6(temb, blk["ada"])
-    n = modulate(layer_norm(x, eps), m[0], m[1])
+    n = _mxq(modulate(layer_norm(x, eps), m[0], m[1]), mx)
     q, k, v = _qkv(n, blk, cfg, dtype)
     o = _merge(attention(q, k, v, key_valid, scale))
     x = x + m[2][:, None, :] * (o @ blk["wo"].T)
-    n = modulate(layer_norm(x, eps), m[3], m[4])
-    return x + m[5][:, None, :] * feed_forward(n, blk["ff1"], blk["ff2"], blk["ff3"])
+    n = _mxq(modulate(layer_norm(x, eps), m[3], m[4]), mx)
+    return x + m[5][:, None, :] * feed_forward(n, blk["ff1"], blk["ff2"], blk["ff3"], mx)
 
 
 def pre_final(temb, x_img, final_ada):
@@ -282,7 +305,7 @@ def embed(cfg: AuraFlowConfig, W: Weights, latents, tau, text, text_mask, dtype=
 
 
 def forward(cfg: AuraFlowConfig, W: Weights, latents, tau, text, text_mask=None,
-            dtype=np.float32, taps=None):
+            dtype=np.float32, taps=None, mx=False):
     """Full transformer forward -> [B, out_channels, H, W].
 
     ``taps(block_index, x_txt, x_img)`` (optional) is called after every block with
@@ -296,13 +319,13 @@ def forward(cfg: AuraFlowConfig, W: Weights, latents, tau, text, text_mask=None,
     for j in range(cfg.num_mmdit_layers):
         x_txt, x_img = joint_block(cfg, _block(W, f"joint{j}.img.", dtype),
                                    _block(W, f"joint{j}.txt.", dtype), temb, x_txt, x_img,
-                                   key_valid, dtype)
+                                   key_valid, dtype, mx)
         if taps is not None:
             taps(bi, x_txt, x_img)
         bi += 1
     x = np.concatenate([x_txt, x_img], axis=1)
     for i in range(cfg.num_single_dit_layers):
-        x = single_block(cfg, _block(W, f"single{i}.", dtype), temb, x, key_valid, dtype)
+        x = single_block(cfg, _block(W, f"single{i}.", dtype), temb, x, key_valid, dtype, mx)
         if taps is not None:
             taps(bi, x[:, :Nt], x[:, Nt:])
         bi += 1
