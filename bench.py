@@ -37,6 +37,8 @@ os.environ.setdefault("OMP_NUM_THREADS", str(_cpu_threads()))
 import numpy as np  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA, published
+MX_CLASSES = ("gemm_qkv", "gemm_ffn_up", "gemm_ffn_down")   # products on MXFP8 operands in --mxfp8 runs
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
 
 WORKLOADS = {
@@ -167,6 +169,8 @@ def main():
                     help="any latent size (even, at most 192 x 192) instead of the workload's square one")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true")
+    ap.add_argument("--mxfp8", action="store_true",
+                    help="MXFP8 model: QKV and FFN products on MXFP8 operands (E4M3, 32-wide block scales)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run the plain 512 MiB device copy used to scale the HBM byte counters")
     args = ap.parse_args()
@@ -192,7 +196,8 @@ def main():
     B, H, W, T = WORKLOADS[args.workload]
     if args.latent:
         H, W = (int(x) for x in args.latent.lower().split("x"))
-    cfg = af.make_config(max_batch=B, max_latent_h=H, max_latent_w=W, max_text_len=T)
+    cfg = af.make_config(max_batch=B, max_latent_h=H, max_latent_w=W, max_text_len=T,
+                         compute_dtype=af.AF_MXFP8 if args.mxfp8 else af.AF_BF16)
     d = cfg.num_attention_heads * cfg.attention_head_dim
     F = ((8 * d) // 3 + 255) // 256 * 256
     L = cfg.num_mmdit_layers + cfg.num_single_dit_layers
@@ -262,8 +267,9 @@ def main():
             if work is not None:
                 rate = work / (kms / n * 1e-3)
                 if kind == "mfma":
+                    peak = PEAK_FP8_TFLOPS if args.mxfp8 and name in MX_CLASSES else PEAK_BF16_TFLOPS
                     entry["tflops"] = rate / 1e12
-                    entry["frac_peak"] = rate / 1e12 / PEAK_BF16_TFLOPS
+                    entry["frac_peak"] = rate / 1e12 / peak
                 else:
                     entry["gbs"] = rate / 1e9
                     entry["frac_peak"] = rate / 1e9 / PEAK_HBM_GBS
@@ -274,9 +280,10 @@ def main():
             name, kms, n, work, kind = best
             avg = kms / n * 1e-3
             if kind == "mfma":
+                peak = PEAK_FP8_TFLOPS if args.mxfp8 and name in MX_CLASSES else PEAK_BF16_TFLOPS
                 roofline = {"bound": "mfma", "kernel": name, "achieved": work / avg / 1e12,
-                            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                            "frac": work / avg / 1e12 / PEAK_BF16_TFLOPS, "traffic": measured_traffic(name),
+                            "peak": peak, "unit": "TFLOP/s", "frac": work / avg / 1e12 / peak,
+                            "traffic": None if args.mxfp8 else measured_traffic(name),
                             "avg_launch_ms": avg * 1e3, "work_per_launch": work}
             else:
                 roofline = {"bound": "hbm", "kernel": name, "achieved": work / avg / 1e9, "peak": PEAK_HBM_GBS,
@@ -299,12 +306,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "mxfp8+bf16" if args.mxfp8 else "bf16",
         "data": "synthetic",
         "config": {"workload": f"AuraFlow transformer forward at {8 * W}x{8 * H} pixels "
                                f"(latent 4x{H}x{W}: {Nimg} image + 8 register + {T} text tokens), CFG batch {B}, "
                                f"4 joint + 32 single blocks, d=3072, 12x256 heads, FFN 8192, seeded random "
-                               f"bf16 weights (6.86B params), padded text masked",
+                               f"bf16 weights (6.86B params), padded text masked"
+                               + (", QKV and FFN products on MXFP8 operands" if args.mxfp8 else ""),
                    "global_batch": B, "seq_len": S, "parallelism": "single GPU"},
         "tflops": tflops,
         "pct_peak_bf16": 100.0 * tflops / PEAK_BF16_TFLOPS,

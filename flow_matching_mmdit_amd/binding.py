@@ -20,7 +20,7 @@ import torch  # noqa: F401
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libauraflow.so")
 
 AF_OK, AF_E_INVALID_ARG, AF_E_SHAPE, AF_E_UNSUPPORTED, AF_E_OOM, AF_E_HIP, AF_E_STATE = range(7)
-AF_F32, AF_BF16 = 0, 1
+AF_F32, AF_BF16, AF_MXFP8 = 0, 1, 2
 
 
 class AfConfig(C.Structure):

@@ -23,6 +23,28 @@ __device__ __forceinline__ uint32_t pack2bf(float lo, float hi) {
 }
 __device__ __forceinline__ bf16_t f2bf(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
 
+// ---- MXFP8 (E4M3 elements with a power-of-two scale per 32 values)
+// Scale exponent of a block whose largest magnitude is amax: floor(log2(amax)) - 8
+// (8 = exponent of E4M3's largest normal, 448), at least -127; amax = 0 (or an
+// fp32 denormal) gives -127. Read from the exponent field, so exact.
+__device__ __forceinline__ int mx_scale_exp(float amax) {
+    const int ef = (int)((__float_as_uint(amax) >> 23) & 255);
+    return ef == 0 ? -127 : max(ef - 127 - 8, -127);
+}
+// 2^k for k in [-126, 127], exact.
+__device__ __forceinline__ float pow2f(int k) { return __uint_as_float((uint32_t)(k + 127) << 23); }
+// Four values -> four E4M3 bytes (round to nearest even; values clamped to
+// +-448 first, since the conversion turns larger magnitudes into NaN).
+__device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float d) {
+    a = fminf(fmaxf(a, -448.f), 448.f);
+    b = fminf(fmaxf(b, -448.f), 448.f);
+    c = fminf(fmaxf(c, -448.f), 448.f);
+    d = fminf(fmaxf(d, -448.f), 448.f);
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+    return (uint32_t)w;
+}
+
 // x * sigmoid(x) with the hardware exponential and a fast (not IEEE-rounded) division.
 __device__ __forceinline__ float silu_f(float x) { return __fdividef(x, 1.0f + __expf(-x)); }
 

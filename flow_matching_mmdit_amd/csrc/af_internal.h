@@ -18,8 +18,10 @@ enum GemmEpi {
 };
 
 struct GemmGroup {
-    const void* A; long lda;   // [M, K] row-major
+    const void* A; long lda;   // [M, K] row-major (MXFP8: bytes per row)
     const void* W; long ldw;   // [N, K] row-major (weights, y = x W^T)
+    const uint8_t* As;         // MXFP8 only: block scales of A, [K/64][as_rows][2] bytes, row 0 of the group
+    const uint8_t* Ws;         // MXFP8 only: block scales of W, [K/64][ws_rows][2] bytes
     int M;
     int row0;                  // residual row of GEMM row 0 (GATED_RESID, QKV)
     int gate_off;              // column of gate vector inside a mod row (GATED_RESID)
@@ -30,7 +32,9 @@ struct GemmLaunch {
     int ngroups;
     int N, K;
     int epi;
-    void* C; long ldc;                 // STORE / SWIGLU output
+    void* C; long ldc;                 // STORE / SWIGLU output (MXFP8 SwiGLU output: fp8, ldc in bytes)
+    uint8_t* Cs; long cs_rows;         // MXFP8 SwiGLU output scales, [F/64][cs_rows][2] bytes
+    long as_rows, ws_rows;             // MXFP8 operands: rows of one K/64 slab of the scale arrays
     float* resid;                      // MAPPED / GATED_RESID output, leading dim N
     const float* mod; long mod_stride; // gate vectors: mod[b * mod_stride + gate_off + n]
     RowGeom geom;
@@ -42,6 +46,9 @@ struct GemmLaunch {
 };
 
 hipError_t gemm_bf16(const GemmLaunch& L, hipStream_t s);
+// MXFP8 operands (E4M3 values, one power-of-two scale per 32 values along K):
+// EPI_QKV, EPI_SWIGLU (MXFP8 output) and EPI_GATED_RESID; K a multiple of 256.
+hipError_t gemm_mxfp8(const GemmLaunch& L, hipStream_t s);
 hipError_t gemm_f32(const GemmLaunch& L, hipStream_t s);
 
 // ------------------------------------------------------------------ attention
@@ -79,6 +86,13 @@ hipError_t key_bias(const uint8_t* mask, int T, int R, RowGeom g, int S_pad, flo
 hipError_t ln_modulate(const float* x, int M, int d, RowGeom g, int split, const float* mod,
                        long mod_stride, int sh_a, int sc_a, int sh_b, int sc_b, void* out,
                        af_dtype odt, float eps, hipStream_t s);
+// MXFP8 variant: fp8 rows out [M, d] (row stride d bytes) and block scales sc
+// [d/64][sc_rows][2]; d a multiple of 256.
+hipError_t ln_modulate_mx(const float* x, int M, int d, RowGeom g, int split, const float* mod, long mod_stride,
+                          int sh_a, int sc_a, int sh_b, int sc_b, uint8_t* out, uint8_t* sc, long sc_rows, float eps,
+                          hipStream_t s);
+// bf16 [N, K] -> MXFP8 [N, K] + scales [K/64][N][2].
+hipError_t mx_quantize_rows(const bf16_t* src, long N, int K, uint8_t* dst, uint8_t* sc, hipStream_t s);
 hipError_t prefinal_project(const float* resid, RowGeom g, int d, const float* mod, long mod_stride,
                             int sc_off, int sh_off, const void* Wout, af_dtype wdt, int Cout, int p,
                             int h, int w, float* out, hipStream_t s);

@@ -57,8 +57,8 @@ af_status derive(const af_config* c, Derived* out) {
         c->num_register_tokens < 0 || c->max_batch < 0 || c->max_latent_h < 0 || c->max_latent_w < 0 ||
         c->max_text_len < 0)
         return fail(AF_E_INVALID_ARG, "config has a negative or zero size");
-    if (c->compute_dtype != AF_F32 && c->compute_dtype != AF_BF16)
-        return fail(AF_E_INVALID_ARG, "compute_dtype must be AF_F32 or AF_BF16");
+    if (c->compute_dtype != AF_F32 && c->compute_dtype != AF_BF16 && c->compute_dtype != AF_MXFP8)
+        return fail(AF_E_INVALID_ARG, "compute_dtype must be AF_F32, AF_BF16 or AF_MXFP8");
     if (!(c->ln_eps > 0.f) || !std::isfinite(c->timestep_scale))
         return fail(AF_E_INVALID_ARG, "ln_eps must be > 0 and timestep_scale finite");
     Derived d{};
@@ -78,7 +78,7 @@ af_status derive(const af_config* c, Derived* out) {
     if (c->in_channels * c->patch_size * c->patch_size > 64 || c->out_channels * c->patch_size * c->patch_size > 64)
         return fail(AF_E_UNSUPPORTED, "patch vectors longer than 64 are not built");
     if (d.d % 4 != 0 || d.d > 4096) return fail(AF_E_UNSUPPORTED, "inner dim must be a multiple of 4 and <= 4096");
-    if (c->compute_dtype == AF_BF16) {
+    if (c->compute_dtype != AF_F32) {
         if (d.hd != 256) return fail(AF_E_UNSUPPORTED, "bf16 path is built for attention_head_dim 256");
         if (d.d % 256 != 0) return fail(AF_E_UNSUPPORTED, "bf16 path needs inner dim % 256 == 0");
         if (c->joint_attention_dim % 64 != 0)
@@ -121,6 +121,9 @@ struct BlockW {
     void* wo;     // [d, d]
     void* ff12;   // [2F, d] gate/up interleaved in 32-row groups
     void* ff3;    // [d, F]
+    // MXFP8 models: E4M3 copies of wqkv, ff12, ff3 and their block scales [K/64][N][2]
+    uint8_t *wqkv8 = nullptr, *wqkv_s = nullptr, *ff12_8 = nullptr, *ff12_s = nullptr, *ff3_8 = nullptr,
+            *ff3_s = nullptr;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -143,8 +146,11 @@ struct af_model {
     af_config cfg;
     Derived D;
     int device;
-    af_dtype dt;
-    size_t es;  // bytes per compute element (2 bf16, 4 fp32)
+    af_dtype dt;     // storage type of weights and activations: AF_BF16 or AF_F32
+    size_t es;       // bytes per compute element (2 bf16, 4 fp32)
+    bool mx = false; // AF_MXFP8: QKV and FFN products on MXFP8 operands
+    bool mx_ready = false;    // the MXFP8 weight copies match the loaded weights
+    void* arena8 = nullptr;   // MXFP8 weight copies
 
     // weights
     std::vector<Slot> slots;
@@ -164,6 +170,10 @@ struct af_model {
     float *mod = nullptr, *temb = nullptr, *hpre = nullptr, *tfeat = nullptr, *kbias = nullptr;
     bf16_t* text_bf16 = nullptr;
     float* attn_part = nullptr;  // partial sums of split attention query tiles (bf16 path)
+    // MXFP8 activations: LN + modulate output [Mp, d], SwiGLU output [Mp, F] (E4M3)
+    // and their block scales [K/64][Mp][2]
+    uint8_t *nrm8 = nullptr, *nrm_s = nullptr, *ffh8 = nullptr, *ffh_s = nullptr;
+    long Mp = 0;                 // rows of the activation buffers (M_max + one tile of padding)
     int n_cu = 0;                // compute units of the device
     float* staging = nullptr;
     size_t staging_floats = 0;
@@ -268,8 +278,8 @@ af_status weight_list(const af_config* c, ListOnly* out) {
     af_model tmp;
     tmp.cfg = *c;
     tmp.D = D;
-    tmp.dt = c->compute_dtype;
-    tmp.es = c->compute_dtype == AF_BF16 ? 2 : 4;
+    tmp.dt = c->compute_dtype == AF_F32 ? AF_F32 : AF_BF16;
+    tmp.es = tmp.dt == AF_BF16 ? 2 : 4;
     build_slots(&tmp);
     out->slots = tmp.slots;
     out->total = tmp.total_floats;
@@ -390,6 +400,7 @@ struct View {
     float* resid;
     void *nrm, *attn, *ffh, *q, *k, *v;
     float *raw, *kbias, *mod;
+    uint8_t *nrm8, *nrm_s, *ffh8, *ffh_s;   // MXFP8 models
 };
 
 View group_view(af_model* m, int b0, int S, int S_pad) {
@@ -408,6 +419,10 @@ View group_view(af_model* m, int b0, int S, int S_pad) {
     V.raw = m->raw ? m->raw + r0 * std::max(3 * D.d, 2 * D.F) : nullptr;
     V.kbias = m->kbias + (size_t)b0 * S_pad;
     V.mod = m->mod + (size_t)b0 * D.mod_cols;
+    V.nrm8 = m->mx ? m->nrm8 + r0 * D.d : nullptr;
+    V.nrm_s = m->mx ? m->nrm_s + r0 * 2 : nullptr;
+    V.ffh8 = m->mx ? m->ffh8 + r0 * D.F : nullptr;
+    V.ffh_s = m->mx ? m->ffh_s + r0 * 2 : nullptr;
     return V;
 }
 
@@ -443,14 +458,56 @@ af_status run_block(af_model* m, const View& V, RowGeom g, int S_pad, const Bloc
     const int split = joint ? Mt : M;
     const long off_a = off_t, off_b = joint ? off_i : off_t;
 
+    // MXFP8 operand groups: rows [0, Mt) and [Mt, M) of an fp8 activation buffer
+    // (row stride K bytes, scales row-offset by 2 bytes per row) with one weight set each
+    auto mx_groups = [&](GemmLaunch& L, const uint8_t* A8, const uint8_t* As, long K, int which) {
+        auto one = [&](const BlockW* w, int Mrows, int r0, long gate_rel, long off) {
+            GemmGroup& G = L.g[L.ngroups++];
+            G.A = A8 + (size_t)r0 * K;
+            G.As = As + (size_t)r0 * 2;
+            G.lda = K;
+            G.W = which == 0 ? w->wqkv8 : which == 2 ? w->ff12_8 : w->ff3_8;
+            G.Ws = which == 0 ? w->wqkv_s : which == 2 ? w->ff12_s : w->ff3_s;
+            G.ldw = K;
+            G.M = Mrows;
+            G.row0 = r0;
+            G.gate_off = (int)(off + gate_rel);
+        };
+        const long gate_rel = which == 3 ? 5 * d : 0;
+        if (joint) {
+            one(wt, Mt, 0, gate_rel, off_t);
+            one(wi, M - Mt, Mt, gate_rel, off_i);
+        } else {
+            one(wt, M, 0, gate_rel, off_t);
+        }
+        L.as_rows = m->Mp;
+        L.ws_rows = which == 0 ? 3 * d : which == 2 ? 2 * F : d;
+    };
+    auto mx_gemm = [&](GemmLaunch& L) {
+        hipError_t e = gemm_mxfp8(L, s);
+        if (e != hipSuccess) return fail(AF_E_HIP, std::string("MXFP8 gemm launch: ") + hipGetErrorString(e));
+        return AF_OK;
+    };
+
     // 1. LN + modulate(shift1, scale1)
     {
     ProfScope ps(m, AF_K_LN_MOD, s);
-    AF_K(ln_modulate(V.resid, M, d, g, split, V.mod, D.mod_cols, off_a, off_a + d, off_b, off_b + d, V.nrm, m->dt,
-                     m->cfg.ln_eps, s));
+    if (m->mx)
+        AF_K(ln_modulate_mx(V.resid, M, d, g, split, V.mod, D.mod_cols, off_a, off_a + d, off_b, off_b + d, V.nrm8,
+                            V.nrm_s, m->Mp, m->cfg.ln_eps, s));
+    else
+        AF_K(ln_modulate(V.resid, M, d, g, split, V.mod, D.mod_cols, off_a, off_a + d, off_b, off_b + d, V.nrm, m->dt,
+                         m->cfg.ln_eps, s));
     }
     // 2. QKV (+ QK-norm)
-    {
+    if (m->mx) {
+        ProfScope ps(m, AF_K_GEMM_QKV, s);
+        GemmLaunch L = gemm_base(m, V.mod, g, 3 * d, d, EPI_QKV);
+        L.q = V.q; L.k = V.k; L.vt = V.v; L.S_pad = S_pad;
+        L.q_scale = ATTN_BF16_Q_SCALE;
+        mx_groups(L, V.nrm8, V.nrm_s, d, 0);
+        AF_TRY(mx_gemm(L));
+    } else {
         ProfScope ps(m, AF_K_GEMM_QKV, s);
         GemmLaunch L = gemm_base(m, V.mod, g, 3 * d, d, m->dt == AF_BF16 ? EPI_QKV : EPI_STORE);
         L.q = V.q; L.k = V.k; L.vt = V.v; L.S_pad = S_pad;
@@ -483,8 +540,31 @@ af_status run_block(af_model* m, const View& V, RowGeom g, int S_pad, const Bloc
     // 5. LN + modulate(shift2, scale2)
     {
     ProfScope ps(m, AF_K_LN_MOD, s);
-    AF_K(ln_modulate(V.resid, M, d, g, split, V.mod, D.mod_cols, off_a + 3 * d, off_a + 4 * d, off_b + 3 * d,
-                     off_b + 4 * d, V.nrm, m->dt, m->cfg.ln_eps, s));
+    if (m->mx)
+        AF_K(ln_modulate_mx(V.resid, M, d, g, split, V.mod, D.mod_cols, off_a + 3 * d, off_a + 4 * d, off_b + 3 * d,
+                            off_b + 4 * d, V.nrm8, V.nrm_s, m->Mp, m->cfg.ln_eps, s));
+    else
+        AF_K(ln_modulate(V.resid, M, d, g, split, V.mod, D.mod_cols, off_a + 3 * d, off_a + 4 * d, off_b + 3 * d,
+                         off_b + 4 * d, V.nrm, m->dt, m->cfg.ln_eps, s));
+    }
+    if (m->mx) {
+        // 6. FFN up: silu(gate) * up -> MXFP8
+        {
+            ProfScope ps(m, AF_K_GEMM_FFN_UP, s);
+            GemmLaunch L = gemm_base(m, V.mod, g, 2 * F, d, EPI_SWIGLU);
+            L.C = V.ffh8; L.ldc = F; L.Cs = V.ffh_s; L.cs_rows = m->Mp;
+            mx_groups(L, V.nrm8, V.nrm_s, d, 2);
+            AF_TRY(mx_gemm(L));
+        }
+        // 7. FFN down, residual += gate2 * (.)
+        {
+            ProfScope ps(m, AF_K_GEMM_FFN_DOWN, s);
+            GemmLaunch L = gemm_base(m, V.mod, g, d, F, EPI_GATED_RESID);
+            L.resid = V.resid;
+            mx_groups(L, V.ffh8, V.ffh_s, F, 3);
+            AF_TRY(mx_gemm(L));
+        }
+        return AF_OK;
     }
     // 6. FFN up: silu(gate) * up
     {
@@ -624,6 +704,7 @@ af_status check_forward_args(af_model* m, const Inputs& in, const void* outp) {
     if (in.B > 0 && (!in.latents || !in.tau || !outp)) return fail(AF_E_INVALID_ARG, "NULL device pointer");
     if (in.B > 0 && in.T > 0 && !in.text) return fail(AF_E_INVALID_ARG, "text_embeds is NULL");
     if (!weights_complete(m)) return fail(AF_E_STATE, "weights not fully loaded");
+    if (m->mx && !m->mx_ready) return fail(AF_E_STATE, "MXFP8 weights not quantized");
     return AF_OK;
 }
 
@@ -702,7 +783,8 @@ af_status af_create(const af_config* c, int device, af_model** out) {
     m->cfg = *c;
     m->D = D;
     m->device = device;
-    m->dt = c->compute_dtype;
+    m->dt = c->compute_dtype == AF_F32 ? AF_F32 : AF_BF16;
+    m->mx = c->compute_dtype == AF_MXFP8;
     m->es = m->dt == AF_BF16 ? 2 : 4;
     build_slots(m);
 
@@ -725,6 +807,23 @@ af_status af_create(const af_config* c, int device, af_model** out) {
             bw.ff12 = bp((int)(intptr_t)bw.ff12);
             bw.ff3 = bp((int)(intptr_t)bw.ff3);
         }
+    if (m->mx) {
+        // E4M3 copies (N x K bytes) and scales (N x K / 32 bytes) of wqkv, ff12, ff3
+        const size_t d_ = D.d, F_ = D.F;
+        const size_t sizes[3] = {3 * d_ * d_, 2 * F_ * d_, d_ * F_};
+        size_t per = 0;
+        for (size_t z : sizes) per += align256(z) + align256(z / 32);
+        const size_t nsets = m->joint_img.size() + m->joint_txt.size() + m->single.size();
+        if (hipMalloc(&m->arena8, per * nsets) != hipSuccess) return cleanup(AF_E_OOM, "MXFP8 weight allocation failed");
+        uint8_t* p8 = (uint8_t*)m->arena8;
+        auto take = [&](size_t z) { uint8_t* r = p8; p8 += align256(z); return r; };
+        for (auto* list : {&m->joint_img, &m->joint_txt, &m->single})
+            for (auto& bw : *list) {
+                bw.wqkv8 = take(sizes[0]); bw.wqkv_s = take(sizes[0] / 32);
+                bw.ff12_8 = take(sizes[1]); bw.ff12_s = take(sizes[1] / 32);
+                bw.ff3_8 = take(sizes[2]); bw.ff3_s = take(sizes[2] / 32);
+            }
+    }
 
     // workspace
     const int p = c->patch_size;
@@ -758,6 +857,13 @@ af_status af_create(const af_config* c, int device, af_model** out) {
     if (hipDeviceGetAttribute(&m->n_cu, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || m->n_cu <= 0)
         return cleanup(AF_E_HIP, "compute-unit count query failed");
     if (m->dt == AF_BF16) ws.push_back({(void**)&m->attn_part, attention_bf16_part_floats(m->n_cu) * 4});
+    m->Mp = Mp;
+    if (m->mx) {
+        ws.push_back({(void**)&m->nrm8, (size_t)Mp * d});
+        ws.push_back({(void**)&m->nrm_s, (size_t)Mp * d / 32});
+        ws.push_back({(void**)&m->ffh8, (size_t)Mp * F});
+        ws.push_back({(void**)&m->ffh_s, (size_t)Mp * F / 32});
+    }
     m->staging_floats = 16u << 20;
     ws.push_back({(void**)&m->staging, m->staging_floats * 4});
     size_t wtotal = 0;
@@ -796,8 +902,22 @@ af_status af_load_weights(af_model* m, const float* host, size_t offset, size_t 
             AF_K(pack_weights(m->staging, (long)cn, (long)(c0 - ts), dst, ddt, S.layout, (int)S.cols, s));
         }
     }
-    AF_HIP(hipStreamSynchronize(s));
     mark_loaded(m, offset, end);
+    if (m->mx) {
+        // MXFP8 models: (re)quantize the block GEMM weights once the list is complete
+        m->mx_ready = false;
+        if (weights_complete(m)) {
+            const long d = m->D.d, F = m->D.F;
+            for (auto* list : {&m->joint_img, &m->joint_txt, &m->single})
+                for (auto& bw : *list) {
+                    AF_K(mx_quantize_rows((const bf16_t*)bw.wqkv, 3 * d, (int)d, bw.wqkv8, bw.wqkv_s, s));
+                    AF_K(mx_quantize_rows((const bf16_t*)bw.ff12, 2 * F, (int)d, bw.ff12_8, bw.ff12_s, s));
+                    AF_K(mx_quantize_rows((const bf16_t*)bw.ff3, d, (int)F, bw.ff3_8, bw.ff3_s, s));
+                }
+            m->mx_ready = true;
+        }
+    }
+    AF_HIP(hipStreamSynchronize(s));
     return AF_OK;
 }
 
@@ -881,6 +1001,7 @@ void af_destroy(af_model* m) {
         }
         if (m->arena) (void)hipFree(m->arena);
         if (m->work) (void)hipFree(m->work);
+        if (m->arena8) (void)hipFree(m->arena8);
     }
     delete m;
 }

@@ -440,6 +440,91 @@ hipError_t ln_modulate(const float* x, int M, int d, RowGeom g, int split, const
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------- MXFP8 output
+// The same LayerNorm + modulate with an MXFP8 output for the MXFP8 GEMMs: each
+// 32 consecutive values of a row share the scale 2^e, e = floor(log2(max |y|)) - 8
+// (at least -127), and are stored as E4M3 bytes of y / 2^e (clamped to +-448,
+// rounded to nearest even); scale bytes e + 127 in the [d/64][sc_rows][2] layout.
+// Lane l holds columns 4 (l + 64 i) .. + 3, so one 32-value block is the 8 lanes
+// 8q .. 8q + 7 of one i.
+template <int MAXV>
+__global__ __launch_bounds__(256) void k_ln_modulate_mx(const float* __restrict__ x, int M, int d, RowGeom g,
+                                                        int split, const float* __restrict__ mod, long mod_stride,
+                                                        int sh_a, int sc_a, int sh_b, int sc_b,
+                                                        uint8_t* __restrict__ out, uint8_t* __restrict__ sc,
+                                                        long sc_rows, float eps) {
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= M) return;
+    const int nv = d / 4;
+    const float* xr = x + (long)row * d;
+    float4 v[MAXV];
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i) {
+        const int c4 = lane + 64 * i;
+        v[i] = c4 < nv ? reinterpret_cast<const float4*>(xr)[c4] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i) sum += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+    const float mean = wave_sum(sum) / (float)d;
+    float sq = 0.f;
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i) {
+        const int c4 = lane + 64 * i;
+        if (c4 < nv) {
+            float a = v[i].x - mean, b = v[i].y - mean, c = v[i].z - mean, e = v[i].w - mean;
+            sq += (a * a + b * b) + (c * c + e * e);
+        }
+    }
+    const float rstd = rsqrtf(wave_sum(sq) / (float)d + eps);
+    const int bidx = g.batch_of(row);
+    const bool first = row < split;
+    const float* shp = mod + (long)bidx * mod_stride + (first ? sh_a : sh_b);
+    const float* scp = mod + (long)bidx * mod_stride + (first ? sc_a : sc_b);
+    uint8_t* orow = out + (long)row * d;
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i) {
+        const int c4 = lane + 64 * i;
+        if (i * 64 < nv) {                   // uniform: d is a multiple of 256
+            const float4 sh = reinterpret_cast<const float4*>(shp)[c4];
+            const float4 s4 = reinterpret_cast<const float4*>(scp)[c4];
+            const float y0 = (v[i].x - mean) * rstd * (1.f + s4.x) + sh.x;
+            const float y1 = (v[i].y - mean) * rstd * (1.f + s4.y) + sh.y;
+            const float y2 = (v[i].z - mean) * rstd * (1.f + s4.z) + sh.z;
+            const float y3 = (v[i].w - mean) * rstd * (1.f + s4.w) + sh.w;
+            float amax = fmaxf(fmaxf(fabsf(y0), fabsf(y1)), fmaxf(fabsf(y2), fabsf(y3)));
+            amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+            amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+            amax = fmaxf(amax, __shfl_xor(amax, 4, 64));
+            const int e = mx_scale_exp(amax);
+            const float inv = pow2f(-e);
+            *reinterpret_cast<uint32_t*>(orow + 4 * c4) = pack4_e4m3(y0 * inv, y1 * inv, y2 * inv, y3 * inv);
+            if ((lane & 7) == 0) {
+                const int blk = c4 >> 3;
+                sc[((long)(blk >> 1) * sc_rows + row) * 2 + (blk & 1)] = (uint8_t)(e + 127);
+            }
+        }
+    }
+}
+
+hipError_t ln_modulate_mx(const float* x, int M, int d, RowGeom g, int split, const float* mod, long mod_stride,
+                          int sh_a, int sc_a, int sh_b, int sc_b, uint8_t* out, uint8_t* sc, long sc_rows, float eps,
+                          hipStream_t s) {
+    if (M == 0) return hipSuccess;
+    if (d % 256 != 0 || d > 4096) return hipErrorInvalidValue;
+    dim3 grid((M + 3) / 4);
+#define AF_LNMX(V) hipLaunchKernelGGL((k_ln_modulate_mx<V>), grid, dim3(256), 0, s, x, M, d, g, split, mod, mod_stride, \
+                                      sh_a, sc_a, sh_b, sc_b, out, sc, sc_rows, eps)
+    const int per_lane = d / 256;
+    if (per_lane <= 4) AF_LNMX(4);
+    else if (per_lane <= 8) AF_LNMX(8);
+    else if (per_lane <= 12) AF_LNMX(12);
+    else AF_LNMX(16);
+#undef AF_LNMX
+    return hipGetLastError();
+}
+
 // ============================================================================ pre-final + proj_out + unpatchify
 // [TRANS] 核心子模块架构 (调制与归一化) and 前向传播流程: y = x (1 + scale) + shift
 // on the image rows (modulation only), z = y W_out^T (no bias), and z's
@@ -567,6 +652,51 @@ hipError_t pack_weights(const float* src, long n, long first, void* dst, af_dtyp
     if (n == 0) return hipSuccess;
     hipLaunchKernelGGL(k_pack, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, src, n, first, dst,
                        ddt == AF_BF16 ? 1 : 0, layout, cols);
+    return hipGetLastError();
+}
+
+// ============================================================================ MXFP8 weights
+// bf16 weight [N, K] -> E4M3 [N, K] + block scales [K/64][N][2] (the MXFP8 rule
+// of the activations: scale 2^(floor(log2 amax) - 8) per 32 values along K). One
+// thread per (row, 32-value block).
+__global__ void k_mx_quant_rows(const bf16_t* __restrict__ src, long N, int K, uint8_t* __restrict__ dst,
+                                uint8_t* __restrict__ sc) {
+    const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    const int nb = K / 32;
+    if (i >= N * nb) return;
+    const long n = i / nb;
+    const int b = (int)(i % nb);
+    const bf16_t* p = src + n * K + b * 32;
+    float v[32];
+    float amax = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint4 u = *reinterpret_cast<const uint4*>(p + 8 * q);
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            v[8 * q + 2 * r] = __uint_as_float(w[r] << 16);
+            v[8 * q + 2 * r + 1] = __uint_as_float(w[r] & 0xFFFF0000u);
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < 32; ++k) amax = fmaxf(amax, fabsf(v[k]));
+    const int e = mx_scale_exp(amax);
+    const float inv = pow2f(-e);
+    uint32_t o[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) o[q] = pack4_e4m3(v[4 * q] * inv, v[4 * q + 1] * inv, v[4 * q + 2] * inv, v[4 * q + 3] * inv);
+    uint4* d4 = reinterpret_cast<uint4*>(dst + n * K + b * 32);
+    d4[0] = make_uint4(o[0], o[1], o[2], o[3]);
+    d4[1] = make_uint4(o[4], o[5], o[6], o[7]);
+    sc[((long)(b >> 1) * N + n) * 2 + (b & 1)] = (uint8_t)(e + 127);
+}
+
+hipError_t mx_quantize_rows(const bf16_t* src, long N, int K, uint8_t* dst, uint8_t* sc, hipStream_t s) {
+    if (N == 0) return hipSuccess;
+    if (K % 64 != 0) return hipErrorInvalidValue;
+    const long n = N * (K / 32);
+    hipLaunchKernelGGL(k_mx_quant_rows, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, src, N, K, dst, sc);
     return hipGetLastError();
 }
 

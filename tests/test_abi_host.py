@@ -143,3 +143,13 @@ def test_forward_rejects_null_model(af):
     st = lib.af_transformer_forward(None, None, None, None, 0, None, 1, 16, 16, 8, None, None)
     assert st == af.AF_E_INVALID_ARG
     assert b"model" in lib.af_last_error()
+
+
+def test_mxfp8_config_checks(af):
+    # host-only: the MXFP8 compute type is accepted with the bf16 constraints
+    af.af_check_shapes(af.make_config(compute_dtype=af.AF_MXFP8), 2, 128, 128, 256)
+    with pytest.raises(ValueError):
+        af.af_check_shapes(af.make_config(compute_dtype=3), 2, 128, 128, 256)
+    with pytest.raises(ValueError):   # head dim other than 256 is not built for the bf16 / MXFP8 paths
+        af.af_check_shapes(af.make_config(compute_dtype=af.AF_MXFP8, attention_head_dim=128,
+                                          caption_projection_dim=1536), 2, 128, 128, 256)
