@@ -62,9 +62,11 @@ hipError_t gemm_f32(const GemmLaunch& L, hipStream_t s);
 constexpr float ATTN_BF16_Q_SCALE = 1.4426950408889634f / 16.0f;
 constexpr float ATTN_BF16_KEY_KEEP = -16.25f * 1.4426950408889634f;
 // part: scratch for split query tiles, attention_bf16_part_floats(n_cu) floats
-// (NULL: no splitting); n_cu: compute units of the device.
+// (NULL: no splitting); n_cu: compute units of the device. o8 != NULL: the output
+// goes to o8 [M, d] as MXFP8 with scales o8s [d/64][sc_rows][2] instead of o.
 hipError_t attention_bf16(const bf16_t* q, const bf16_t* k, const bf16_t* vt, const float* bias,
-                          RowGeom g, int H, int S_pad, bf16_t* o, int d, int n_cu, float* part, hipStream_t s);
+                          RowGeom g, int H, int S_pad, bf16_t* o, int d, int n_cu, float* part, uint8_t* o8,
+                          uint8_t* o8s, long sc_rows, hipStream_t s);
 size_t attention_bf16_part_floats(int n_cu);
 hipError_t attention_f32(const float* q, const float* k, const float* v, const float* bias,
                          RowGeom g, int H, int hd, int S_pad, float* o, int d, hipStream_t s);

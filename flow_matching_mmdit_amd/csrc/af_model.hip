@@ -121,9 +121,9 @@ struct BlockW {
     void* wo;     // [d, d]
     void* ff12;   // [2F, d] gate/up interleaved in 32-row groups
     void* ff3;    // [d, F]
-    // MXFP8 models: E4M3 copies of wqkv, ff12, ff3 and their block scales [K/64][N][2]
-    uint8_t *wqkv8 = nullptr, *wqkv_s = nullptr, *ff12_8 = nullptr, *ff12_s = nullptr, *ff3_8 = nullptr,
-            *ff3_s = nullptr;
+    // MXFP8 models: E4M3 copies of wqkv, wo, ff12, ff3 and their block scales [K/64][N][2]
+    uint8_t *wqkv8 = nullptr, *wqkv_s = nullptr, *wo8 = nullptr, *wo_s = nullptr, *ff12_8 = nullptr,
+            *ff12_s = nullptr, *ff3_8 = nullptr, *ff3_s = nullptr;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -148,7 +148,7 @@ struct af_model {
     int device;
     af_dtype dt;     // storage type of weights and activations: AF_BF16 or AF_F32
     size_t es;       // bytes per compute element (2 bf16, 4 fp32)
-    bool mx = false; // AF_MXFP8: QKV and FFN products on MXFP8 operands
+    bool mx = false; // AF_MXFP8: QKV, out-projection and FFN products on MXFP8 operands
     bool mx_ready = false;    // the MXFP8 weight copies match the loaded weights
     void* arena8 = nullptr;   // MXFP8 weight copies
 
@@ -170,9 +170,10 @@ struct af_model {
     float *mod = nullptr, *temb = nullptr, *hpre = nullptr, *tfeat = nullptr, *kbias = nullptr;
     bf16_t* text_bf16 = nullptr;
     float* attn_part = nullptr;  // partial sums of split attention query tiles (bf16 path)
-    // MXFP8 activations: LN + modulate output [Mp, d], SwiGLU output [Mp, F] (E4M3)
-    // and their block scales [K/64][Mp][2]
-    uint8_t *nrm8 = nullptr, *nrm_s = nullptr, *ffh8 = nullptr, *ffh_s = nullptr;
+    // MXFP8 activations: LN + modulate output [Mp, d], attention output [Mp, d],
+    // SwiGLU output [Mp, F] (E4M3) and their block scales [K/64][Mp][2]
+    uint8_t *nrm8 = nullptr, *nrm_s = nullptr, *attn8 = nullptr, *attn_s = nullptr, *ffh8 = nullptr,
+            *ffh_s = nullptr;
     long Mp = 0;                 // rows of the activation buffers (M_max + one tile of padding)
     int n_cu = 0;                // compute units of the device
     float* staging = nullptr;
@@ -400,7 +401,7 @@ struct View {
     float* resid;
     void *nrm, *attn, *ffh, *q, *k, *v;
     float *raw, *kbias, *mod;
-    uint8_t *nrm8, *nrm_s, *ffh8, *ffh_s;   // MXFP8 models
+    uint8_t *nrm8, *nrm_s, *attn8, *attn_s, *ffh8, *ffh_s;   // MXFP8 models
 };
 
 View group_view(af_model* m, int b0, int S, int S_pad) {
@@ -421,6 +422,8 @@ View group_view(af_model* m, int b0, int S, int S_pad) {
     V.mod = m->mod + (size_t)b0 * D.mod_cols;
     V.nrm8 = m->mx ? m->nrm8 + r0 * D.d : nullptr;
     V.nrm_s = m->mx ? m->nrm_s + r0 * 2 : nullptr;
+    V.attn8 = m->mx ? m->attn8 + r0 * D.d : nullptr;
+    V.attn_s = m->mx ? m->attn_s + r0 * 2 : nullptr;
     V.ffh8 = m->mx ? m->ffh8 + r0 * D.F : nullptr;
     V.ffh_s = m->mx ? m->ffh_s + r0 * 2 : nullptr;
     return V;
@@ -466,14 +469,14 @@ af_status run_block(af_model* m, const View& V, RowGeom g, int S_pad, const Bloc
             G.A = A8 + (size_t)r0 * K;
             G.As = As + (size_t)r0 * 2;
             G.lda = K;
-            G.W = which == 0 ? w->wqkv8 : which == 2 ? w->ff12_8 : w->ff3_8;
-            G.Ws = which == 0 ? w->wqkv_s : which == 2 ? w->ff12_s : w->ff3_s;
+            G.W = which == 0 ? w->wqkv8 : which == 1 ? w->wo8 : which == 2 ? w->ff12_8 : w->ff3_8;
+            G.Ws = which == 0 ? w->wqkv_s : which == 1 ? w->wo_s : which == 2 ? w->ff12_s : w->ff3_s;
             G.ldw = K;
             G.M = Mrows;
             G.row0 = r0;
             G.gate_off = (int)(off + gate_rel);
         };
-        const long gate_rel = which == 3 ? 5 * d : 0;
+        const long gate_rel = which == 3 ? 5 * d : which == 1 ? 2 * d : 0;
         if (joint) {
             one(wt, Mt, 0, gate_rel, off_t);
             one(wi, M - Mt, Mt, gate_rel, off_i);
@@ -481,7 +484,7 @@ af_status run_block(af_model* m, const View& V, RowGeom g, int S_pad, const Bloc
             one(wt, M, 0, gate_rel, off_t);
         }
         L.as_rows = m->Mp;
-        L.ws_rows = which == 0 ? 3 * d : which == 2 ? 2 * F : d;
+        L.ws_rows = which == 0 ? 3 * d : which == 2 ? 2 * F : d;   // wo and ff3 have d rows
     };
     auto mx_gemm = [&](GemmLaunch& L) {
         hipError_t e = gemm_mxfp8(L, s);
@@ -524,13 +527,19 @@ af_status run_block(af_model* m, const View& V, RowGeom g, int S_pad, const Bloc
     ProfScope ps(m, AF_K_ATTENTION, s);
     if (m->dt == AF_BF16)
         AF_K(attention_bf16((const bf16_t*)V.q, (const bf16_t*)V.k, (const bf16_t*)V.v, V.kbias, g, D.H, S_pad,
-                            (bf16_t*)V.attn, d, m->n_cu, m->attn_part, s));
+                            (bf16_t*)V.attn, d, m->n_cu, m->attn_part, V.attn8, V.attn_s, m->Mp, s));
     else
         AF_K(attention_f32((const float*)V.q, (const float*)V.k, (const float*)V.v, V.kbias, g, D.H, D.hd, S_pad,
                            (float*)V.attn, d, s));
     }
     // 4. out projection, residual += gate1 * (.)
-    {
+    if (m->mx) {
+        ProfScope ps(m, AF_K_GEMM_OUT, s);
+        GemmLaunch L = gemm_base(m, V.mod, g, d, d, EPI_GATED_RESID);
+        L.resid = V.resid;
+        mx_groups(L, V.attn8, V.attn_s, d, 1);
+        AF_TRY(mx_gemm(L));
+    } else {
         ProfScope ps(m, AF_K_GEMM_OUT, s);
         GemmLaunch L = gemm_base(m, V.mod, g, d, d, EPI_GATED_RESID);
         L.resid = V.resid;
@@ -808,9 +817,9 @@ af_status af_create(const af_config* c, int device, af_model** out) {
             bw.ff3 = bp((int)(intptr_t)bw.ff3);
         }
     if (m->mx) {
-        // E4M3 copies (N x K bytes) and scales (N x K / 32 bytes) of wqkv, ff12, ff3
+        // E4M3 copies (N x K bytes) and scales (N x K / 32 bytes) of wqkv, wo, ff12, ff3
         const size_t d_ = D.d, F_ = D.F;
-        const size_t sizes[3] = {3 * d_ * d_, 2 * F_ * d_, d_ * F_};
+        const size_t sizes[4] = {3 * d_ * d_, d_ * d_, 2 * F_ * d_, d_ * F_};
         size_t per = 0;
         for (size_t z : sizes) per += align256(z) + align256(z / 32);
         const size_t nsets = m->joint_img.size() + m->joint_txt.size() + m->single.size();
@@ -820,8 +829,9 @@ af_status af_create(const af_config* c, int device, af_model** out) {
         for (auto* list : {&m->joint_img, &m->joint_txt, &m->single})
             for (auto& bw : *list) {
                 bw.wqkv8 = take(sizes[0]); bw.wqkv_s = take(sizes[0] / 32);
-                bw.ff12_8 = take(sizes[1]); bw.ff12_s = take(sizes[1] / 32);
-                bw.ff3_8 = take(sizes[2]); bw.ff3_s = take(sizes[2] / 32);
+                bw.wo8 = take(sizes[1]); bw.wo_s = take(sizes[1] / 32);
+                bw.ff12_8 = take(sizes[2]); bw.ff12_s = take(sizes[2] / 32);
+                bw.ff3_8 = take(sizes[3]); bw.ff3_s = take(sizes[3] / 32);
             }
     }
 
@@ -861,6 +871,8 @@ af_status af_create(const af_config* c, int device, af_model** out) {
     if (m->mx) {
         ws.push_back({(void**)&m->nrm8, (size_t)Mp * d});
         ws.push_back({(void**)&m->nrm_s, (size_t)Mp * d / 32});
+        ws.push_back({(void**)&m->attn8, (size_t)Mp * d});
+        ws.push_back({(void**)&m->attn_s, (size_t)Mp * d / 32});
         ws.push_back({(void**)&m->ffh8, (size_t)Mp * F});
         ws.push_back({(void**)&m->ffh_s, (size_t)Mp * F / 32});
     }
@@ -911,6 +923,7 @@ af_status af_load_weights(af_model* m, const float* host, size_t offset, size_t 
             for (auto* list : {&m->joint_img, &m->joint_txt, &m->single})
                 for (auto& bw : *list) {
                     AF_K(mx_quantize_rows((const bf16_t*)bw.wqkv, 3 * d, (int)d, bw.wqkv8, bw.wqkv_s, s));
+                    AF_K(mx_quantize_rows((const bf16_t*)bw.wo, d, (int)d, bw.wo8, bw.wo_s, s));
                     AF_K(mx_quantize_rows((const bf16_t*)bw.ff12, 2 * F, (int)d, bw.ff12_8, bw.ff12_s, s));
                     AF_K(mx_quantize_rows((const bf16_t*)bw.ff3, d, (int)F, bw.ff3_8, bw.ff3_s, s));
                 }

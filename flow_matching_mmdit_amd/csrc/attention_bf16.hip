@@ -7,7 +7,8 @@
 //
 // Layout: q, k [B, H, S_pad, 256]; v^T [B, H, 256, S_pad] (written transposed by
 // the QKV GEMM epilogue so the P V contraction reads keys contiguously);
-// output o [M, d] in residual-row order.
+// output o [M, d] in residual-row order, bf16, or MXFP8 (E4M3 values plus one
+// power-of-two scale per 32 head-dim values) for the MXFP8 out-projection.
 //
 // Scaled inputs: q arrives multiplied by log2(e)/16 (the QKV epilogue applies
 // it before rounding to bf16) and the key bias holds -16.25 log2(e) for a kept
@@ -63,7 +64,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_attention_bf16(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
                       const bf16_t* __restrict__ Vt, const float* __restrict__ bias, RowGeom g, int H,
                       int S_pad, bf16_t* __restrict__ O, int d, int nqt, int nfull, int kp,
-                      float* __restrict__ part) {
+                      float* __restrict__ part, uint8_t* __restrict__ O8, uint8_t* __restrict__ O8s, long sc_rows) {
     // K slot 0, K slot 1, v^T slot 0, v^T slot 1, then per slot and wave a 1 KB
     // bias block (4 copies of 64 fp32 keys)
     __shared__ __attribute__((aligned(1024))) bf16_t smem[4 * KTILE + 2 * 4 * 512];
@@ -334,6 +335,31 @@ void k_attention_bf16(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K
     // ---- normalise and store
     const float inv = 1.f / l_tot;
     const int q = q0 + l32;
+    if (O8) {
+        // MXFP8 output: head-dim block ht (32 values) is held by lanes l and l ^ 32
+        const long row = q < S ? g.row_of(b, q) : 0;
+#pragma unroll
+        for (int ht = 0; ht < 8; ++ht) {
+            float amax = 0.f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(o[ht][r] * inv));
+            amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+            const int e = mx_scale_exp(amax);
+            const float sc = inv * pow2f(-e);
+            if (q < S) {
+                uint8_t* orow = O8 + row * d + h * HD + ht * 32 + grp * 4;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    *reinterpret_cast<uint32_t*>(orow + i * 8) =
+                        pack4_e4m3(o[ht][i * 4 + 0] * sc, o[ht][i * 4 + 1] * sc, o[ht][i * 4 + 2] * sc, o[ht][i * 4 + 3] * sc);
+                if (grp == 0) {
+                    const int blk = h * 8 + ht;
+                    O8s[((long)(blk >> 1) * sc_rows + row) * 2 + (blk & 1)] = (uint8_t)(e + 127);
+                }
+            }
+        }
+        return;
+    }
     if (q < S) {
         bf16_t* orow = O + (long)g.row_of(b, q) * d + h * HD + grp * 4;
 #pragma unroll
@@ -351,7 +377,8 @@ void k_attention_bf16(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K
 // One wave per query: lane l holds head dims [4 l, 4 l + 4).
 __global__ __launch_bounds__(256) void k_attention_combine(const float* __restrict__ part, int nfull, int kp,
                                                            int ntail, int nqt, int H, RowGeom g,
-                                                           bf16_t* __restrict__ O, int d) {
+                                                           bf16_t* __restrict__ O, int d, uint8_t* __restrict__ O8,
+                                                           uint8_t* __restrict__ O8s, long sc_rows) {
     const int lane = threadIdx.x & 63;
     const int w = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
     if (w >= ntail * QT) return;
@@ -369,14 +396,32 @@ __global__ __launch_bounds__(256) void k_attention_combine(const float* __restri
         l += blk[QT * HD + ql];
     }
     const float inv = 1.f / l;
-    *reinterpret_cast<uint2*>(O + (long)g.row_of(b, q) * d + h * HD + lane * 4) =
+    const long row = g.row_of(b, q);
+    if (O8) {
+        // MXFP8 output: one 32-value block = 8 consecutive lanes
+        const float y0 = acc.x * inv, y1 = acc.y * inv, y2 = acc.z * inv, y3 = acc.w * inv;
+        float amax = fmaxf(fmaxf(fabsf(y0), fabsf(y1)), fmaxf(fabsf(y2), fabsf(y3)));
+        amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+        amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+        amax = fmaxf(amax, __shfl_xor(amax, 4, 64));
+        const int e = mx_scale_exp(amax);
+        const float sc = pow2f(-e);
+        *reinterpret_cast<uint32_t*>(O8 + row * d + h * HD + lane * 4) = pack4_e4m3(y0 * sc, y1 * sc, y2 * sc, y3 * sc);
+        if ((lane & 7) == 0) {
+            const int blk = h * 8 + (lane >> 3);
+            O8s[((long)(blk >> 1) * sc_rows + row) * 2 + (blk & 1)] = (uint8_t)(e + 127);
+        }
+        return;
+    }
+    *reinterpret_cast<uint2*>(O + row * d + h * HD + lane * 4) =
         make_uint2(pack2bf(acc.x * inv, acc.y * inv), pack2bf(acc.z * inv, acc.w * inv));
 }
 
 size_t attention_bf16_part_floats(int n_cu) { return (size_t)n_cu * (QT * HD + QT); }
 
 hipError_t attention_bf16(const bf16_t* q, const bf16_t* k, const bf16_t* vt, const float* bias, RowGeom g, int H,
-                          int S_pad, bf16_t* o, int d, int n_cu, float* part, hipStream_t s) {
+                          int S_pad, bf16_t* o, int d, int n_cu, float* part, uint8_t* o8, uint8_t* o8s,
+                          long sc_rows, hipStream_t s) {
     const int S = g.S();
     if (g.B == 0 || S == 0) return hipSuccess;
     const int nqt = (S + QT - 1) / QT, ntiles = (S + KT - 1) / KT;
@@ -390,12 +435,12 @@ hipError_t attention_bf16(const bf16_t* q, const bf16_t* k, const bf16_t* vt, co
     if (kp < 2) tail = 0, kp = 1;
     const int nfull = total - tail;
     hipLaunchKernelGGL(k_attention_bf16, dim3(nfull + tail * kp), dim3(256), 0, s, q, k, vt, bias, g, H, S_pad, o, d,
-                       nqt, nfull, kp, part);
+                       nqt, nfull, kp, part, o8, o8s, sc_rows);
     if (tail) {
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(k_attention_combine, dim3((tail * QT * 64 + 255) / 256), dim3(256), 0, s, part, nfull, kp,
-                           tail, nqt, H, g, o, d);
+                           tail, nqt, H, g, o, d, o8, o8s, sc_rows);
     }
     return hipGetLastError();
 }

@@ -55,15 +55,16 @@ typedef enum { AF_F32 = 0, AF_BF16 = 1, AF_MXFP8 = 2 } af_dtype;
  * compute_dtype AF_BF16: bf16 weights (the position table stays fp32), fp32
  * accumulation, fp32 norm statistics and residual stream. Requires
  * attention_head_dim == 256, d % 256 == 0 and joint_attention_dim % 64 == 0.
- * compute_dtype AF_MXFP8: the AF_BF16 model with the QKV projection and both
- * FFN products computed on MXFP8 operands (the MI355X counterpart of the 8-bit
- * weight variants in [PIPE] 量化加载：用 bitsandbytes 将模型压到 8-bit): their
- * weights, the LayerNorm + modulate outputs feeding them and the SiLU-gated
- * hidden activations are stored as E4M3 values with one power-of-two scale per
+ * compute_dtype AF_MXFP8: the AF_BF16 model with the QKV projection, the
+ * out-projection and both FFN products computed on MXFP8 operands (the MI355X
+ * counterpart of the 8-bit weight variants in [PIPE] 量化加载：用 bitsandbytes
+ * 将模型压到 8-bit): their weights, the LayerNorm + modulate outputs and the
+ * attention output feeding them and the SiLU-gated hidden activations are
+ * stored as E4M3 values with one power-of-two scale per
  * 32 values along the contraction axis (scale 2^(floor(log2(max |x|)) - 8),
  * values clamped to +-448 and rounded to nearest even), multiplied on the fp8
- * matrix cores with fp32 accumulation. Attention, the out-projection and
- * everything else stay as in AF_BF16. The weights are loaded as for AF_BF16;
+ * matrix cores with fp32 accumulation. Attention itself and everything else
+ * stay as in AF_BF16. The weights are loaded as for AF_BF16;
  * the library quantizes them once the whole list is loaded. Requires, in
  * addition, d % 256 == 0.
  * compute_dtype AF_F32: everything fp32; requires attention_head_dim <= 64

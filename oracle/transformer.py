@@ -194,12 +194,13 @@ def _mod6(temb, ada):
     return np.split(m, 6, axis=1)
 
 
-# MXFP8 block GEMMs (mx=True): the QKV projection and both FFN products take
-# MXFP8 operands -- the LayerNorm + modulate output, the SiLU-gated hidden
-# activations and the weights of those three products are quantized along their
-# contraction axis (mxfp8_qdq) and the products accumulate in the working
-# precision. The out-projection, attention and everything else are unchanged.
-MX_WEIGHTS = ("wq", "wk", "wv", "ff1", "ff2", "ff3")
+# MXFP8 block GEMMs (mx=True): the QKV projection, the out-projection and both
+# FFN products take MXFP8 operands -- the LayerNorm + modulate outputs, the
+# attention output, the SiLU-gated hidden activations and the weights of those
+# four products are quantized along their contraction axis (mxfp8_qdq) and the
+# products accumulate in the working precision. Attention itself and everything
+# else are unchanged.
+MX_WEIGHTS = ("wq", "wk", "wv", "wo", "ff1", "ff2", "ff3")
 
 
 def mx_block(blk):
@@ -240,7 +241,7 @@ def joint_block(cfg, blk_img, blk_txt, temb, x_txt, x_img, key_valid, dtype=np.f
     qt, kt, vt = _qkv(n_txt, blk_txt, cfg, dtype)
     o = attention(np.concatenate([qt, qi], axis=2), np.concatenate([kt, ki], axis=2),
                   np.concatenate([vt, vi], axis=2), key_valid, scale)
-    o = _merge(o)
+    o = _mxq(_merge(o), mx)
     o_txt, o_img = o[:, :Nt], o[:, Nt:]
     x_img = x_img + mi[2][:, None, :] * (o_img @ blk_img["wo"].T)
     x_txt = x_txt + mt[2][:, None, :] * (o_txt @ blk_txt["wo"].T)
@@ -264,7 +265,7 @@ def single_block(cfg, blk, temb, x, key_valid, dtype=np.float32, mx=False):
     m = _mod6(temb, blk["ada"])
     n = _mxq(modulate(layer_norm(x, eps), m[0], m[1]), mx)
     q, k, v = _qkv(n, blk, cfg, dtype)
-    o = _merge(attention(q, k, v, key_valid, scale))
+    o = _mxq(_merge(attention(q, k, v, key_valid, scale)), mx)
     x = x + m[2][:, None, :] * (o @ blk["wo"].T)
     n = _mxq(modulate(layer_norm(x, eps), m[3], m[4]), mx)
     return x + m[5][:, None, :] * feed_forward(n, blk["ff1"], blk["ff2"], blk["ff3"], mx)

@@ -119,9 +119,8 @@ def test_mxfp8_qdq_invariants():
 
 
 def test_mx_forward_uses_quantized_operands_only_where_stated():
-    """mx=True changes the block output by MXFP8-sized amounts, only through the QKV
-    and FFN products: with those weights replaced by their quantized values and the
-    activations already on the MXFP8 grid, the two modes agree on an identity-like case."""
+    """mx=True changes the block output by MXFP8-sized amounts; mx_block quantizes
+    exactly the weights of the QKV, out-projection and FFN products."""
     cfg = oracle.TINY
     W = oracle.Weights.seeded(cfg, seed=0)
     rng = np.random.default_rng(3)
@@ -136,6 +135,8 @@ def test_mx_forward_uses_quantized_operands_only_where_stated():
     rel = np.abs(b - a).max() / np.abs(a - x).max()
     assert 1e-4 < rel < 0.1, rel                      # quantization is visible but small
     qb = oracle.mx_block(blk)
-    assert all(np.array_equal(qb[k], blk[k]) for k in ("ada", "wo"))
-    assert not np.array_equal(qb["wq"], blk["wq"])
+    assert np.array_equal(qb["ada"], blk["ada"])
+    for k in ("wq", "wk", "wv", "wo", "ff1", "ff2", "ff3"):
+        assert not np.array_equal(qb[k], blk[k])
+        np.testing.assert_array_equal(qb[k], oracle.mxfp8_qdq(blk[k]))
     np.testing.assert_array_equal(oracle.mxfp8_qdq(qb["ff3"]), qb["ff3"])
