@@ -231,11 +231,13 @@ __global__ __launch_bounds__(256) void k_patch_embed(const float* __restrict__ l
     const int b = blockIdx.z;
     const int t0 = blockIdx.y * PE_ROWS;
     const int c = blockIdx.x * blockDim.x + threadIdx.x;
-    for (int i = threadIdx.x; i < PE_ROWS * Pd; i += blockDim.x) {
-        int r = i / Pd, f = i % Pd;
+    // every one of the PE_MAXF columns is written (zero past Pd): the dot product
+    // below runs over all of them, and 0 times a stale non-finite LDS word is NaN
+    for (int i = threadIdx.x; i < PE_ROWS * PE_MAXF; i += blockDim.x) {
+        int r = i / PE_MAXF, f = i % PE_MAXF;
         int t = t0 + r;
         float v = 0.f;
-        if (t < ntok) {
+        if (t < ntok && f < Pd) {
             int ti = t / w, tj = t % w;
             int ch = f / (p * p), py = (f / p) % p, px = f % p;
             v = lat[(((long)b * C + ch) * H + ti * p + py) * W + tj * p + px];

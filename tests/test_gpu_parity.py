@@ -207,6 +207,23 @@ def test_small_bf16_zero_gates_reduce_to_embed_and_project(af):
     m.close()
 
 
+def test_small_bf16_embedding_stable_after_masked_attention(af, small_bf16):
+    """Regression: the patch embedding once read LDS columns past C p^2 that it never
+    wrote (times a zero weight); the masked attention leaves -inf key biases in LDS,
+    so the embedding turned NaN after enough forwards. Interleave the two and check
+    that the embedding tap stays finite and bit-identical."""
+    torch = _torch()
+    cfg, m, dev, ref, taps, _ = small_bf16
+    first = m.forward_taps(*dev, stop_after_block=-1).cpu().numpy()
+    assert np.isfinite(first).all()
+    for i in range(24):
+        m.forward(*dev)
+        again = m.forward_taps(*dev, stop_after_block=-1).cpu().numpy()
+        assert np.isfinite(again).all(), i
+        np.testing.assert_array_equal(again, first)
+    torch.cuda.synchronize()
+
+
 # ============================================================================ config B: full-width block pair
 
 @pytest.fixture(scope="module")
