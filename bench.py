@@ -136,12 +136,12 @@ def cpu_baseline(shape, threads):
     t0 = time.time()
     cache = {n: Wseed[n] for n in names + blk_names}
     gen_s = time.time() - t0
-    W = oracle.Weights.from_dict(cfg, cache)
+    Wt = oracle.Weights.from_dict(cfg, cache)
     f32 = np.float32
     t0 = time.time()
-    temb, xt, xi, kv = oracle.embed(cfg, W, lat, tau, text, mask, f32)
+    temb, xt, xi, kv = oracle.embed(cfg, Wt, lat, tau, text, mask, f32)
     t_embed = time.time() - t0
-    blk = lambda p: {k: W[p + k] for k in ("ada", "wq", "wk", "wv", "wo", "ff1", "ff2", "ff3")}
+    blk = lambda p: {k: Wt[p + k] for k in ("ada", "wq", "wk", "wv", "wo", "ff1", "ff2", "ff3")}
     t0 = time.time()
     xt2, xi2 = oracle.joint_block(cfg, blk("joint0.img."), blk("joint0.txt."), temb, xt, xi, kv, f32)
     t_joint = time.time() - t0
@@ -170,7 +170,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true")
     ap.add_argument("--mxfp8", action="store_true",
-                    help="MXFP8 model: QKV and FFN products on MXFP8 operands (E4M3, 32-wide block scales)")
+                    help="time the MXFP8 model (QKV, out-projection and FFN products on MXFP8 operands) as the main line")
+    ap.add_argument("--no-mxfp8-leg", action="store_true",
+                    help="skip the extra MXFP8-model timing reported beside the bf16 line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run the plain 512 MiB device copy used to scale the HBM byte counters")
     args = ap.parse_args()
@@ -290,6 +292,30 @@ def main():
                             "unit": "GB/s", "frac": work / avg / 1e9 / PEAK_HBM_GBS, "traffic": measured_traffic(name),
                             "avg_launch_ms": avg * 1e3, "work_per_launch": work}
 
+    # Beside the bf16 line: the same workload on the MXFP8 model (QKV, out-projection
+    # and FFN products on MXFP8 operands), timed the same way; reported as its own
+    # object, never as `value`.
+    mx_leg = None
+    if not args.mxfp8 and not args.no_mxfp8_leg:
+        model.close()
+        del model
+        torch.cuda.synchronize()
+        cfg8 = af.make_config(max_batch=B, max_latent_h=H, max_latent_w=W, max_text_len=T, compute_dtype=af.AF_MXFP8)
+        model = af.AuraFlowModel(cfg8, 0)
+        model.load_seeded_weights(seed=0, threads=_cpu_threads())
+        for _ in range(args.warmup):
+            model.forward(lat, tau, text, mask, out=out)
+        torch.cuda.synchronize()
+        check_finite("MXFP8 warm-up")
+        ms8 = timed(args.steps)
+        check_finite("the MXFP8 timed forwards")
+        print(f"[bench] MXFP8 model: {ms8:.2f} ms/forward", file=sys.stderr, flush=True)
+        mx_leg = {"ms_per_step": ms8, "value": 1000.0 / ms8, "unit": "forwards/s",
+                  "tflops": flops / (ms8 * 1e-3) / 1e12,
+                  "note": "same workload; QKV, out-projection and FFN products on MXFP8 operands (E4M3 values, "
+                          "one power-of-two scale per 32 along K), attention and the rest bf16/fp32; "
+                          "TFLOP/s counts the dense model FLOPs"}
+
     cpu = None
     if not args.no_cpu_baseline:
         print(f"[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
@@ -318,6 +344,7 @@ def main():
         "pct_peak_bf16": 100.0 * tflops / PEAK_BF16_TFLOPS,
         "flops_per_forward": flops,
         "roofline": roofline,
+        "mxfp8_model": mx_leg,
         "cpu_baseline": cpu,
         "kernels": kernels,
         "setup_s": setup_s,
