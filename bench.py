@@ -159,6 +159,62 @@ def cpu_baseline(shape, threads):
     }
 
 
+def sampling_loop_bench(args, af, torch):
+    """25 Euler steps (shift 1.73, guidance 3.5) for 4 images at 1024^2: each step is one
+    transformer forward over [4 uncond; 4 cond] and one CFG + Euler update. Wall time per
+    loop from HIP events around whole loops (sigma schedule computed on the host inside)."""
+    import seeded_inputs
+    imgs, H, W, T, steps = 4, 128, 128, 256, 25
+    B = 2 * imgs
+    cfg = af.make_config(max_batch=B, max_latent_h=H, max_latent_w=W, max_text_len=T,
+                         compute_dtype=af.AF_MXFP8 if args.mxfp8 else af.AF_BF16)
+    d = cfg.num_attention_heads * cfg.attention_head_dim
+    F = ((8 * d) // 3 + 255) // 256 * 256
+    L = cfg.num_mmdit_layers + cfg.num_single_dit_layers
+    Nimg = (H // 2) * (W // 2)
+    S = cfg.num_register_tokens + T + Nimg
+    model = af.AuraFlowModel(cfg, 0)
+    model.load_seeded_weights(seed=0, threads=_cpu_threads())
+    x0 = torch.from_numpy(seeded_inputs.latents(imgs, 4, H, W)).cuda()
+    text = torch.from_numpy(seeded_inputs.text_embeddings(B, T, cfg.joint_attention_dim)).cuda()
+    mask = torch.from_numpy(seeded_inputs.length_mask(seeded_inputs.valid_lengths(B, 16, T), T)).cuda()
+    x = torch.empty_like(x0)
+    stream = torch.cuda.current_stream()
+
+    def loop():
+        x.copy_(x0)
+        model.sample(x, text, mask, num_steps=steps, shift=1.73, guidance=3.5)
+
+    for _ in range(args.warmup):
+        loop()
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(x).all()), "non-finite latents after the warm-up loop"
+    print("[bench] sampling-loop warm-up done", file=sys.stderr, flush=True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        loop()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(x).all()), "non-finite latents after the timed loops"
+    ms = e0.elapsed_time(e1) / args.steps
+    flops = steps * forward_flops(d, F, L, B, S, T, cfg.joint_attention_dim, Nimg, 16)
+    print(json.dumps({
+        "metric": "25-step CFG sampling loop, 4 images at 1024² (transformer batch 8)",
+        "value": imgs * 1000.0 / ms, "unit": "images/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "mxfp8+bf16" if args.mxfp8 else "bf16", "data": "synthetic",
+        "config": {"workload": "flow-matching Euler sampling, 25 steps, shift 1.73, guidance 3.5, 4 images "
+                               "at 1024x1024 (latent 4x128x128), [4 uncond; 4 cond] per forward, seeded random "
+                               "weights and text, padded text masked; a step is one whole 25-step loop",
+                   "global_batch": B, "seq_len": S, "parallelism": "single GPU"},
+        "tflops": flops / (ms * 1e-3) / 1e12,
+        "pct_peak_bf16": 100.0 * flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+    }))
+    model.close()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -173,6 +229,9 @@ def main():
                     help="time the MXFP8 model (QKV, out-projection and FFN products on MXFP8 operands) as the main line")
     ap.add_argument("--no-mxfp8-leg", action="store_true",
                     help="skip the extra MXFP8-model timing reported beside the bf16 line")
+    ap.add_argument("--sampling-loop", action="store_true",
+                    help="time the 25-step flow-matching Euler + CFG sampling loop for 4 images at 1024^2 "
+                         "(transformer batch 8) instead of single forwards; --steps counts loops")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run the plain 512 MiB device copy used to scale the HBM byte counters")
     args = ap.parse_args()
@@ -195,6 +254,9 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.sampling_loop:
+        sampling_loop_bench(args, af, torch)
+        return
     B, H, W, T = WORKLOADS[args.workload]
     if args.latent:
         H, W = (int(x) for x in args.latent.lower().split("x"))
@@ -235,16 +297,25 @@ def main():
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
+    per_fwd = []
+
     def timed(n):
+        # outer events bracket the n forwards; one event between consecutive forwards
+        # (no synchronisation) gives the per-forward spread
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
         torch.cuda.synchronize()
         e0.record(stream)
-        for _ in range(n):
+        ev[0].record(stream)
+        for i in range(n):
             model.forward(lat, tau, text, mask, out=out)
+            ev[i + 1].record(stream)
         e1.record(stream)
         torch.cuda.synchronize()
+        per_fwd[:] = [ev[i].elapsed_time(ev[i + 1]) for i in range(n)]
         return e0.elapsed_time(e1) / n
 
     ms_per_step = timed(args.steps)
+    pct = {f"p{q}": float(np.percentile(per_fwd, q)) for q in (10, 50, 90)}
     value = 1000.0 / ms_per_step
     flops = forward_flops(d, F, L, B, S, T, cfg.joint_attention_dim, Nimg, 16)
     tflops = flops / (ms_per_step * 1e-3) / 1e12
@@ -342,6 +413,7 @@ def main():
                    "global_batch": B, "seq_len": S, "parallelism": "single GPU"},
         "tflops": tflops,
         "pct_peak_bf16": 100.0 * tflops / PEAK_BF16_TFLOPS,
+        "forward_ms_percentiles": pct,
         "flops_per_forward": flops,
         "roofline": roofline,
         "mxfp8_model": mx_leg,

@@ -28,6 +28,15 @@ COMMON = [
 ]
 
 
+# Per-file flags. The attention kernel keeps its MFMA accumulators in VGPRs
+# (its S scores feed VALU exponentials); left to the default heuristic the
+# compiler holds them in AGPRs and shuttles output tiles between the two files
+# every key tile (about 128 copies per 64 keys).
+PER_FILE = {
+    "attention_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def _hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -55,7 +64,8 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
     objs = [os.path.join(BUILD, os.path.basename(s)[:-4] + ".o") for s in srcs]
     jobs = jobs or min(len(srcs), max(1, min(8, os.cpu_count() or 1)))
     with cf.ThreadPoolExecutor(jobs) as ex:
-        futs = [ex.submit(_run, [hipcc, *COMMON, "-c", s, "-o", o]) for s, o in zip(srcs, objs)]
+        futs = [ex.submit(_run, [hipcc, *COMMON, *PER_FILE.get(os.path.basename(s), []), "-c", s, "-o", o])
+                for s, o in zip(srcs, objs)]
         for f in futs:
             out = f.result()
             if verbose and out.strip():
