@@ -160,6 +160,27 @@ def test_small_bf16_blocks_match_oracle(af, small_bf16):
     assert e <= BF16_TOL and c >= BF16_COS, (e, c)
 
 
+def test_small_bf16_single_sample_odd_rows(af, small_bf16):
+    """One sample with S = 8 + 12 + 165 = 185 rows: an odd row count, so every
+    row-tiled kernel ends on a ragged last row."""
+    torch = _torch()
+    cfg, m, _, _, _, _ = small_bf16
+    ocfg = oracle_cfg(cfg)
+    W_o = oracle.Weights.seeded(ocfg, seed=0, bf16=True)
+    lat, taus, text, mask = workload_inputs(1, 4, 22, 30, 12, 128, lengths=[7], cfg_pairs=False)
+    text = oracle.round_bf16(text)
+    ref, taps = _taps_ref(ocfg, W_o, lat, taus, text, mask, np.float32)
+    dev = (to_dev(lat), to_dev(taus), to_dev(text), to_dev(mask))
+    got = {blk: m.forward_taps(*dev, stop_after_block=blk).cpu().numpy() for blk in (0, 1, 2)}
+    out = m.forward(*dev).cpu().numpy()
+    torch.cuda.synchronize()
+    for blk in (0, 1, 2):
+        e, c = rel_max(got[blk], taps[blk]), cosine(got[blk], taps[blk])
+        assert e <= BF16_TOL and c >= BF16_COS, (blk, e, c)
+    e, c = rel_max(out, ref), cosine(out, ref)
+    assert e <= BF16_TOL and c >= BF16_COS, (e, c)
+
+
 def test_small_bf16_deterministic_and_mask_invariant(af, small_bf16):
     torch = _torch()
     cfg, m, dev, ref, taps, host = small_bf16
