@@ -16,6 +16,8 @@ Sources (the web pages this follows), cited by tag throughout:
   [TRANS] "Diffusers 中的 AuraFlowTransformer2DModel：架构解析与源码级使用指南"
   [DEEP]  "【深度拆解】AuraFlow从基座到技术实现：开源文生图新范式"
 
+The pipeline's text encoder (UMT5, a random-weight workload) is in oracle/umt5.py.
+
 Parity status. Every function is pinned by the CPU tests (tests/test_oracle_*.py)
 against closed forms, invariants, brute force on tiny inputs or values the pages
 print. The pages print no worked numeric example of a forward pass, so agreement

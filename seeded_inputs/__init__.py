@@ -16,6 +16,8 @@ Seed roles used by the tests and the bench:
     2 text embeddings (index = sample)
     3 valid text lengths (index = sample)
     4 timesteps (index = sample)
+    5 text-encoder weights (index = position in the encoder's weight list)
+    6 token ids (index = sample)
 """
 from __future__ import annotations
 
@@ -26,18 +28,22 @@ SEED_LATENTS = 1
 SEED_TEXT = 2
 SEED_LENGTHS = 3
 SEED_TIMESTEPS = 4
+SEED_ENCODER_WEIGHTS = 5
+SEED_TOKENS = 6
 
 
 def _gen(seed: int, index: int) -> np.random.Generator:
     return np.random.Generator(np.random.PCG64(np.random.SeedSequence([int(seed), int(index)])))
 
 
-def normal(seed: int, index: int, shape, std: float = 1.0) -> np.ndarray:
-    """float32 array of N(0, std^2) draws for stream (seed, index)."""
+def normal(seed: int, index: int, shape, std: float = 1.0, mean: float = 0.0) -> np.ndarray:
+    """float32 array of N(mean, std^2) draws for stream (seed, index)."""
     g = _gen(seed, index)
     a = g.standard_normal(size=tuple(int(s) for s in shape), dtype=np.float32)
     if std != 1.0:
         a *= np.float32(std)
+    if mean != 0.0:
+        a += np.float32(mean)
     return a
 
 
@@ -86,3 +92,11 @@ def timesteps_uniform(batch: int, low: float = 0.0, high: float = 1000.0,
                       seed: int = SEED_TIMESTEPS) -> np.ndarray:
     """[batch] float64 timesteps t, uniform in [low, high)."""
     return np.array([uniform(seed, b, low, high) for b in range(batch)], np.float64)
+
+
+def token_ids(batch: int, tokens: int, vocab: int, seed: int = SEED_TOKENS) -> np.ndarray:
+    """[batch, tokens] int32 ids, each uniform in [0, vocab); sample b uses stream b."""
+    out = np.empty((batch, tokens), np.int32)
+    for b in range(batch):
+        out[b] = _gen(seed, b).integers(0, vocab, size=tokens)
+    return out
