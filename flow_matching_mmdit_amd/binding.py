@@ -39,12 +39,21 @@ class AfConfig(C.Structure):
         return {k: getattr(self, k) for k, _ in self._fields_}
 
 
+class AfUmt5Config(C.Structure):
+    _fields_ = [
+        ("d_model", C.c_int), ("num_heads", C.c_int), ("num_layers", C.c_int), ("d_ff", C.c_int),
+        ("vocab_size", C.c_int), ("rel_buckets", C.c_int), ("rel_max_distance", C.c_int), ("eps", C.c_float),
+        ("max_batch", C.c_int), ("max_tokens", C.c_int),
+    ]
+
+
 def _load():
     if not os.path.exists(_LIB_PATH):
         raise ImportError(f"{_LIB_PATH} is missing: build it with python -m flow_matching_mmdit_amd.build")
     lib = C.CDLL(_LIB_PATH)
     P, I, SZ, F, D, V = C.c_void_p, C.c_int, C.c_size_t, C.c_float, C.c_double, None
     cfgp = C.POINTER(AfConfig)
+    ucfgp = C.POINTER(AfUmt5Config)
     sig = {
         "af_config_default": (I, [cfgp]),
         "af_check_shapes": (I, [cfgp, I, I, I, I]),
@@ -60,6 +69,15 @@ def _load():
         "af_destroy": (V, [P]),
         "af_status_string": (C.c_char_p, [I]),
         "af_last_error": (C.c_char_p, []),
+        "af_umt5_config_default": (I, [ucfgp]),
+        "af_umt5_weight_count": (I, [ucfgp, C.POINTER(I), C.POINTER(SZ)]),
+        "af_umt5_weight_info": (I, [ucfgp, I, C.c_char_p, I, C.POINTER(C.c_int64), C.POINTER(C.c_int64),
+                                    C.POINTER(SZ)]),
+        "af_umt5_create": (I, [ucfgp, I, C.POINTER(P)]),
+        "af_umt5_load_weights": (I, [P, P, SZ, SZ, P]),
+        "af_umt5_encode": (I, [P, P, P, I, I, P, P]),
+        "af_umt5_encode_taps": (I, [P, P, P, I, I, I, P, P]),
+        "af_umt5_destroy": (V, [P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -73,7 +91,8 @@ EXPORTED = (
     "af_config_default", "af_check_shapes", "af_weight_count", "af_weight_info", "af_create",
     "af_load_weights", "af_init_weights", "af_transformer_forward", "af_transformer_forward_taps",
     "af_flow_euler_cfg_step", "af_sigma_schedule", "af_destroy", "af_status_string",
-    "af_last_error")
+    "af_last_error", "af_umt5_config_default", "af_umt5_weight_count", "af_umt5_weight_info",
+    "af_umt5_create", "af_umt5_load_weights", "af_umt5_encode", "af_umt5_encode_taps", "af_umt5_destroy")
 
 
 class AfError(RuntimeError):
@@ -289,3 +308,119 @@ def af_profile_read(model: "AuraFlowModel") -> dict:
         _check(_lib.af_profile_read(model._h, i, C.byref(ms), C.byref(n)))
         out[name] = (ms.value, n.value)
     return out
+
+
+# ----------------------------------------------------------------------------- text encoder (UMT5)
+
+def umt5_make_config(**kw) -> AfUmt5Config:
+    """The pages' encoder configuration with any field overridden by keyword."""
+    c = AfUmt5Config()
+    _check(_lib.af_umt5_config_default(C.byref(c)))
+    for k, v in kw.items():
+        if not hasattr(c, k):
+            raise KeyError(k)
+        setattr(c, k, v)
+    return c
+
+
+def af_umt5_weight_count(cfg: AfUmt5Config):
+    n, tot = C.c_int(), C.c_size_t()
+    _check(_lib.af_umt5_weight_count(C.byref(cfg), C.byref(n), C.byref(tot)))
+    return n.value, tot.value
+
+
+def af_umt5_weight_info(cfg: AfUmt5Config, index: int):
+    name = C.create_string_buffer(128)
+    r, c, o = C.c_int64(), C.c_int64(), C.c_size_t()
+    _check(_lib.af_umt5_weight_info(C.byref(cfg), index, name, 128, C.byref(r), C.byref(c), C.byref(o)))
+    return name.value.decode(), r.value, c.value, o.value
+
+
+def umt5_weight_recipe(name: str):
+    """Synthetic init recipe (std, mean): embedding N(0, 1); norm weights N(1, 0.1^2);
+    q and k projections N(0, 0.01^2); relative-position tables N(0, 0.5^2); every
+    other matrix N(0, 0.02^2)."""
+    t = name.split(".")[-1]
+    if t == "embed":
+        return 1.0, 0.0
+    if t in ("ln1", "ln2", "final_ln"):
+        return 0.1, 1.0
+    if t in ("wq", "wk"):
+        return 0.01, 0.0
+    if t == "rel_bias":
+        return 0.5, 0.0
+    return 0.02, 0.0
+
+
+class UMT5Encoder:
+    """One text-encoder handle on one device; token ids in, embeddings out."""
+
+    def __init__(self, cfg: AfUmt5Config, device: int = 0):
+        self.cfg = cfg
+        self.device = device
+        h = C.c_void_p()
+        _check(_lib.af_umt5_create(C.byref(cfg), device, C.byref(h)))
+        self._h = h
+        n, total = af_umt5_weight_count(cfg)
+        self.weights = [af_umt5_weight_info(cfg, i) for i in range(n)]
+        self.total_floats = total
+
+    def close(self):
+        if getattr(self, "_h", None):
+            _lib.af_umt5_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def load_weights(self, host: np.ndarray, offset: int = 0, stream=None):
+        a = np.ascontiguousarray(host, dtype=np.float32).ravel()
+        _check(_lib.af_umt5_load_weights(self._h, C.c_void_p(a.ctypes.data), offset, a.size, _stream_ptr(stream)))
+
+    def load_seeded_weights(self, seed: int | None = None, threads: int = 8):
+        """Draws every canonical tensor from seeded_inputs (stream (seed, index)) and loads it."""
+        import seeded_inputs
+        seed = seeded_inputs.SEED_ENCODER_WEIGHTS if seed is None else seed
+
+        def draw(i):
+            name, rows, cols, off = self.weights[i]
+            std, mean = umt5_weight_recipe(name)
+            return off, seeded_inputs.normal(seed, i, (rows, cols) if cols > 1 else (rows,), std, mean)
+
+        n = len(self.weights)
+        win = 2 * max(1, threads)
+        with ThreadPoolExecutor(max(1, threads)) as ex:
+            for w0 in range(0, n, win):
+                for off, a in ex.map(draw, range(w0, min(n, w0 + win))):
+                    self.load_weights(a, off)
+
+    def _args(self, ids, mask):
+        import torch
+        assert ids.dtype == torch.int32 and ids.is_contiguous() and ids.is_cuda and ids.dim() == 2
+        B, T = ids.shape
+        mptr = None
+        if mask is not None:
+            assert mask.dtype == torch.uint8 and mask.is_contiguous() and tuple(mask.shape) == (B, T)
+            mptr = C.c_void_p(mask.data_ptr())
+        return B, T, mptr
+
+    def encode(self, ids, mask=None, out=None, stream=None):
+        import torch
+        B, T, mptr = self._args(ids, mask)
+        if out is None:
+            out = torch.empty((B, T, self.cfg.d_model), dtype=torch.float32, device=ids.device)
+        _check(_lib.af_umt5_encode(self._h, C.c_void_p(ids.data_ptr()), mptr, B, T, C.c_void_p(out.data_ptr()),
+                                   _stream_ptr(stream)))
+        return out
+
+    def encode_taps(self, ids, mask=None, stop_after_layer: int = 0, out=None, stream=None):
+        import torch
+        B, T, mptr = self._args(ids, mask)
+        if out is None:
+            out = torch.empty((B, T, self.cfg.d_model), dtype=torch.float32, device=ids.device)
+        _check(_lib.af_umt5_encode_taps(self._h, C.c_void_p(ids.data_ptr()), mptr, B, T, stop_after_layer,
+                                        C.c_void_p(out.data_ptr()), _stream_ptr(stream)))
+        return out

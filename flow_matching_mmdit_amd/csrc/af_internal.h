@@ -14,7 +14,8 @@ enum GemmEpi {
     EPI_STORE_MAPPED = 1,   // resid[map(m), n] = acc (fp32), map = (m/seg_len)*seg_stride + seg_off + m%seg_len
     EPI_GATED_RESID = 2,    // resid[row0 + m, n] += gate[batch(row0 + m), n] * acc
     EPI_QKV = 3,            // bf16 only: per-head LayerNorm of q, k; q, k -> [B,H,S_pad,hd]; v -> v^T [B,H,hd,S_pad]
-    EPI_SWIGLU = 4          // bf16 only: h[m, f] = silu(acc[gate col]) * acc[up col], 32-column interleave
+    EPI_SWIGLU = 4,         // bf16 only: h[m, f] = silu(acc[gate col]) * acc[up col], 32-column interleave
+    EPI_GEGLU = 5           // bf16 only: as SWIGLU with the tanh-form GELU in place of silu (text encoder)
 };
 
 struct GemmGroup {
@@ -108,5 +109,20 @@ hipError_t taps_permute(const float* resid, RowGeom g, int d, float* out, hipStr
 hipError_t qknorm_scatter_f32(const float* raw, int M, RowGeom g, int H, int hd, int S_pad,
                               float eps, float* q, float* k, float* v, int row0, hipStream_t s);
 hipError_t swiglu_f32(const float* raw, int M, int F, float* h, hipStream_t s);
+
+// ------------------------------------------------------------------ text encoder (UMT5)
+hipError_t umt5_embed(const int32_t* ids, long M, const bf16_t* E, int vocab, int d, float* x, hipStream_t s);
+// out = x / sqrt(mean(x^2) + eps) * w per row; bf16 or fp32 output
+hipError_t umt5_rms_norm(const float* x, int M, int d, const float* w, float eps, void* out, bool bf16_out,
+                         hipStream_t s);
+// rows[l][h][rel + T - 1] = rel_bias[l][bucket(rel)][h] (32 buckets, max distance 128)
+hipError_t umt5_rel_bias_rows(const float* rel_bias, int L, int H, int T, float* rows, hipStream_t s);
+// qkv [B*T (+ padding), 3d] bf16 (q | k | v column blocks, head h at h*64); bias_rows [H][2T-1];
+// out [B*T, d] bf16; T <= 512
+hipError_t umt5_attention(const bf16_t* qkv, int B, int T, int H, int d, const float* bias_rows,
+                          const uint8_t* mask, bf16_t* out, hipStream_t s);
+
+// Records `msg` as this thread's last error (af_last_error) and returns s.
+af_status report(af_status s, const char* msg);
 
 }  // namespace af

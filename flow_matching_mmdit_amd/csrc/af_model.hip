@@ -22,6 +22,17 @@ af_status fail(af_status s, const std::string& msg) {
     return s;
 }
 
+}  // namespace
+
+// Shared with the other executors (the text encoder): records the message read
+// back by af_last_error on this thread.
+af_status af::report(af_status s, const char* msg) {
+    g_last_error = msg;
+    return s;
+}
+
+namespace {
+
 #define AF_HIP(call)                                                                        \
     do {                                                                                    \
         hipError_t e_ = (call);                                                             \

@@ -10,6 +10,7 @@
 //                  [B, H, S_pad, 256] and v to v^T [B, H, 256, S_pad]
 //   SWIGLU         silu(gate) * up of the interleaved FFN columns
 //                  ([PIPE] 深入源码, 前馈网络)
+//   GEGLU          the same with the tanh-form GELU (the text encoder's gated FFN)
 //
 // Tiling: 256 x 256 block tile, eight waves (two per SIMD) in a 4 x 2
 // arrangement, each wave owning a 64 x 128 sub-tile (2 x 4 MFMA tiles, 128 fp32
@@ -176,7 +177,7 @@ void k_gemm_bf16(GemmLaunch L) {
     };
     // q and k tiles of the QKV GEMM and the SwiGLU tiles run in the row-major
     // (C^T) orientation; everything else in the column-major one.
-    if constexpr (EPI == EPI_SWIGLU) {
+    if constexpr (EPI == EPI_SWIGLU || EPI == EPI_GEGLU) {
         mainloop(Orient<true>{});
     } else if constexpr (EPI == EPI_QKV) {
         if (n0 / (L.N / 3) < 2) mainloop(Orient<true>{});
@@ -210,6 +211,7 @@ hipError_t gemm_bf16(const GemmLaunch& L, hipStream_t s) {
             break;
         case EPI_QKV: hipLaunchKernelGGL((k_gemm_bf16<EPI_QKV, GEMM_WM, GEMM_WN>), grid, block, 0, s, LL); break;
         case EPI_SWIGLU: hipLaunchKernelGGL((k_gemm_bf16<EPI_SWIGLU, GEMM_WM, GEMM_WN>), grid, block, 0, s, LL); break;
+        case EPI_GEGLU: hipLaunchKernelGGL((k_gemm_bf16<EPI_GEGLU, GEMM_WM, GEMM_WN>), grid, block, 0, s, LL); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -227,7 +227,7 @@ __device__ __forceinline__ void epilogue(const GemmLaunch& L, f32x16 (&acc)[BM /
                 *reinterpret_cast<uint4*>(Hout + (long)(row0 + m) * L.ldc + fcol0 + ch * 16) = v;
             }
         }
-    } else if constexpr (EPI == EPI_SWIGLU) {
+    } else if constexpr (EPI == EPI_SWIGLU || EPI == EPI_GEGLU) {
         // h tile [256 rows][128 cols] bf16 staged in LDS, then 16-byte row stores.
         // Row-major orientation: gate block nt = 2p and up block 2p + 1 give h
         // columns wn*64 + p*32 + i*8 + grp*4 + j, four of them per 8-byte write.
@@ -240,7 +240,10 @@ __device__ __forceinline__ void epilogue(const GemmLaunch& L, f32x16 (&acc)[BM /
                 for (int i = 0; i < 4; ++i) {
                     float h[4];
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) h[j] = silu_f(acc[mt][2 * p2][i * 4 + j]) * acc[mt][2 * p2 + 1][i * 4 + j];
+                    for (int j = 0; j < 4; ++j) {
+                        const float g = acc[mt][2 * p2][i * 4 + j];
+                        h[j] = (EPI == EPI_GEGLU ? gelu_tanh_f(g) : silu_f(g)) * acc[mt][2 * p2 + 1][i * 4 + j];
+                    }
                     *reinterpret_cast<uint2*>(st + (rr_row + mt * 32) * HS + wn * (TN / 2) + p2 * 32 + i * 8 +
                                               (lane >> 5) * 4) = make_uint2(pack2bf(h[0], h[1]), pack2bf(h[2], h[3]));
                 }

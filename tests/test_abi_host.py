@@ -14,9 +14,13 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def _declared():
-    text = open(os.path.join(ROOT, "include", "auraflow.h")).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(af_[a-z_0-9]+)\s*\(", text)))
+    names = set()
+    for h in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if h.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", h)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names |= set(re.findall(r"\b(af_[a-z_0-9]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_symbol(af):
@@ -153,3 +157,38 @@ def test_mxfp8_config_checks(af):
     with pytest.raises(ValueError):   # head dim other than 256 is not built for the bf16 / MXFP8 paths
         af.af_check_shapes(af.make_config(compute_dtype=af.AF_MXFP8, attention_head_dim=128,
                                           caption_projection_dim=1536), 2, 128, 128, 256)
+
+
+# ----------------------------------------------------------------------------- text encoder (UMT5)
+
+def test_umt5_weight_list_matches_oracle(af):
+    from oracle import umt5 as U
+    for ocfg, kw in ((U.UMT5_FULL, {}), (U.UMT5_SMALL, dict(d_model=256, num_heads=4, num_layers=2, d_ff=512,
+                                                            vocab_size=1000))):
+        cfg = af.umt5_make_config(**kw)
+        n, total = af.af_umt5_weight_count(cfg)
+        specs = U.umt5_weight_specs(ocfg)
+        assert n == len(specs)
+        off = 0
+        for i, (name, shape, std, mean) in enumerate(specs):
+            nm, r, c, o = af.af_umt5_weight_info(cfg, i)
+            assert nm == name and o == off, (i, nm, name)
+            assert (r, c) == (shape[0], shape[1] if len(shape) > 1 else 1)
+            assert af.umt5_weight_recipe(nm) == (std, mean), nm
+            off += int(np.prod(shape))
+        assert total == off
+
+
+@pytest.mark.parametrize("kw", [dict(num_heads=16), dict(d_model=2176, num_heads=34), dict(d_ff=5000),
+                                dict(rel_buckets=64), dict(rel_max_distance=64), dict(max_tokens=513),
+                                dict(eps=0.0), dict(vocab_size=0)])
+def test_umt5_config_checks(af, kw):
+    with pytest.raises(ValueError):
+        af.af_umt5_weight_count(af.umt5_make_config(**kw))
+
+
+def test_umt5_default_config_matches_pages(af):
+    c = af.umt5_make_config()
+    # [DEEP] 2.1 文本编码器: d_model 2048, 32 heads, 24 layers, d_ff 5120, vocab 32128, max distance 128
+    assert (c.d_model, c.num_heads, c.num_layers, c.d_ff, c.vocab_size, c.rel_max_distance) == \
+        (2048, 32, 24, 5120, 32128, 128)
