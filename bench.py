@@ -159,6 +159,42 @@ def cpu_baseline(shape, threads):
     }
 
 
+def text_encoder_leg(args, af, torch, steps, warmup):
+    """The pipeline's text encoder (UMT5: 24 layers, d_model 2048, 32 heads of 64, d_ff 5120,
+    vocabulary 32128) on 8 prompts x 256 tokens (a CFG batch of 4 images: 4 prompts and 4
+    negative prompts), random bf16 weights, ragged valid lengths. Returns the timing object."""
+    import seeded_inputs
+    B, T = 8, 256
+    cfg = af.umt5_make_config(max_batch=B, max_tokens=T)
+    d, F, L = cfg.d_model, cfg.d_ff, cfg.num_layers
+    enc = af.UMT5Encoder(cfg, 0)
+    enc.load_seeded_weights(threads=_cpu_threads())
+    ids = torch.from_numpy(seeded_inputs.token_ids(B, T, cfg.vocab_size)).cuda()
+    mask = torch.from_numpy(seeded_inputs.length_mask(seeded_inputs.valid_lengths(B, 16, T), T)).cuda()
+    out = torch.empty((B, T, d), dtype=torch.float32, device="cuda")
+    for _ in range(warmup):
+        enc.encode(ids, mask, out=out)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out).all()), "non-finite text-encoder output"
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        enc.encode(ids, mask, out=out)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    M = B * T
+    flops = L * (2.0 * M * d * 3 * d + 2.0 * M * d * d + 2.0 * M * d * 2 * F + 2.0 * M * F * d + 4.0 * B * T * T * d)
+    enc.close()
+    return {"workload": f"UMT5 text encoder, {L} layers, d_model {d}, {cfg.num_heads} heads of 64, d_ff {F}, "
+                        f"vocabulary {cfg.vocab_size}; {B} prompts x {T} tokens, ragged valid lengths; seeded "
+                        f"random bf16 weights",
+            "ms_per_encode": ms, "value": 1000.0 / ms, "unit": "encodes/s", "flops_per_encode": flops,
+            "tflops": flops / (ms * 1e-3) / 1e12, "pct_peak_bf16": 100.0 * flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+
+
 def sampling_loop_bench(args, af, torch):
     """25 Euler steps (shift 1.73, guidance 3.5) for 4 images at 1024^2: each step is one
     transformer forward over [4 uncond; 4 cond] and one CFG + Euler update. Wall time per
@@ -232,6 +268,10 @@ def main():
     ap.add_argument("--sampling-loop", action="store_true",
                     help="time the 25-step flow-matching Euler + CFG sampling loop for 4 images at 1024^2 "
                          "(transformer batch 8) instead of single forwards; --steps counts loops")
+    ap.add_argument("--text-encoder", action="store_true",
+                    help="time only the text encoder (8 prompts x 256 tokens) and print its own line")
+    ap.add_argument("--no-text-encoder-leg", action="store_true",
+                    help="skip the text-encoder timing reported beside the transformer line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run the plain 512 MiB device copy used to scale the HBM byte counters")
     args = ap.parse_args()
@@ -256,6 +296,16 @@ def main():
     torch.cuda.set_device(0)
     if args.sampling_loop:
         sampling_loop_bench(args, af, torch)
+        return
+    if args.text_encoder:
+        leg = text_encoder_leg(args, af, torch, args.steps, args.warmup)
+        print(json.dumps({"metric": "UMT5 text-encoder encodes/s (8 prompts x 256 tokens)", "value": leg["value"],
+                          "unit": "encodes/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                          "ms_per_step": leg["ms_per_encode"], "higher_is_better": True, "scaling": "weak",
+                          "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+                          "config": {"workload": leg["workload"], "global_batch": 8, "seq_len": 256,
+                                     "parallelism": "single GPU"},
+                          "tflops": leg["tflops"], "pct_peak_bf16": leg["pct_peak_bf16"]}))
         return
     B, H, W, T = WORKLOADS[args.workload]
     if args.latent:
@@ -387,6 +437,14 @@ def main():
                           "one power-of-two scale per 32 along K), attention and the rest bf16/fp32; "
                           "TFLOP/s counts the dense model FLOPs"}
 
+    te = None
+    if not args.no_text_encoder_leg and not args.mxfp8:
+        model.close()
+        del model
+        torch.cuda.synchronize()
+        te = text_encoder_leg(args, af, torch, args.steps, args.warmup)
+        print(f"[bench] text encoder: {te['ms_per_encode']:.2f} ms/encode", file=sys.stderr, flush=True)
+
     cpu = None
     if not args.no_cpu_baseline:
         print(f"[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
@@ -417,6 +475,7 @@ def main():
         "flops_per_forward": flops,
         "roofline": roofline,
         "mxfp8_model": mx_leg,
+        "text_encoder": te,
         "cpu_baseline": cpu,
         "kernels": kernels,
         "setup_s": setup_s,
