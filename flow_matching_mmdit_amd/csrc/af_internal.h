@@ -15,7 +15,9 @@ enum GemmEpi {
     EPI_GATED_RESID = 2,    // resid[row0 + m, n] += gate[batch(row0 + m), n] * acc
     EPI_QKV = 3,            // bf16 only: per-head LayerNorm of q, k; q, k -> [B,H,S_pad,hd]; v -> v^T [B,H,hd,S_pad]
     EPI_SWIGLU = 4,         // bf16 only: h[m, f] = silu(acc[gate col]) * acc[up col], 32-column interleave
-    EPI_GEGLU = 5           // bf16 only: as SWIGLU with the tanh-form GELU in place of silu (text encoder)
+    EPI_GEGLU = 5,          // bf16 only: as SWIGLU with the tanh-form GELU in place of silu (text encoder)
+    EPI_PARTIAL = 6         // bf16 only, one group: split-K partial sums, C = fp32 [ksplit][M][N]; split s
+                            // covers K columns [s K/ksplit, (s+1) K/ksplit); splitk_resid adds them up
 };
 
 struct GemmGroup {
@@ -44,6 +46,7 @@ struct GemmLaunch {
     int H, hd, S_pad;
     float eps;
     float q_scale;                     // QKV: factor on the normalised q before rounding (1 = none)
+    int ksplit;                        // PARTIAL: number of K ranges (K a multiple of 32 ksplit)
 };
 
 hipError_t gemm_bf16(const GemmLaunch& L, hipStream_t s);
@@ -121,6 +124,9 @@ hipError_t umt5_rel_bias_rows(const float* rel_bias, int L, int H, int T, float*
 // out [B*T, d] bf16; T <= 512
 hipError_t umt5_attention(const bf16_t* qkv, int B, int T, int H, int d, const float* bias_rows,
                           const uint8_t* mask, bf16_t* out, hipStream_t s);
+
+// resid[m, n] += sum over s = 0 .. ks-1, in that order, of part[s][m][n] (the EPI_PARTIAL output)
+hipError_t splitk_resid(const float* part, int ks, long M, int N, float* resid, hipStream_t s);
 
 // Records `msg` as this thread's last error (af_last_error) and returns s.
 af_status report(af_status s, const char* msg);

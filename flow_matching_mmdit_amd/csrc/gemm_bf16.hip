@@ -11,6 +11,8 @@
 //   SWIGLU         silu(gate) * up of the interleaved FFN columns
 //                  ([PIPE] 深入源码, 前馈网络)
 //   GEGLU          the same with the tanh-form GELU (the text encoder's gated FFN)
+//   PARTIAL        fp32 partial sums over one of ksplit K ranges (split-K for
+//                  launches with few tiles; splitk_resid adds them in order)
 //
 // Tiling: 256 x 256 block tile, eight waves (two per SIMD) in a 4 x 2
 // arrangement, each wave owning a 64 x 128 sub-tile (2 x 4 MFMA tiles, 128 fp32
@@ -49,15 +51,23 @@ void k_gemm_bf16(GemmLaunch L) {
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WN, wn = wave % WN;
 
-    const TileMap tmap = tile_map(L);
+    // PARTIAL: the launch repeats the tile set once per K range
+    int bid = blockIdx.x, split = 0;
+    if constexpr (EPI == EPI_PARTIAL) {
+        const int T = tiles_m(L.g[0].M) * (L.N / BN);
+        split = bid / T;
+        bid -= split * T;
+    }
+    const TileMap tmap = tile_map(L, bid);
     const int gi = tmap.gi;
-    const bf16_t* __restrict__ A = (const bf16_t*)(gi ? L.g[1].A : L.g[0].A);
     const long lda = gi ? L.g[1].lda : L.g[0].lda;
-    const bf16_t* __restrict__ W = (const bf16_t*)(gi ? L.g[1].W : L.g[0].W);
     const long ldw = gi ? L.g[1].ldw : L.g[0].ldw;
-    const int M = tmap.M, row0 = tmap.row0, gate_off = tmap.gate_off;
+    const int K = EPI == EPI_PARTIAL ? L.K / L.ksplit : L.K;
+    const bf16_t* __restrict__ A = (const bf16_t*)(gi ? L.g[1].A : L.g[0].A) + (long)split * K;
+    const bf16_t* __restrict__ W = (const bf16_t*)(gi ? L.g[1].W : L.g[0].W) + (long)split * K;
+    const int M = tmap.M, gate_off = tmap.gate_off;
+    const int row0 = EPI == EPI_PARTIAL ? split * M : tmap.row0;
     const int m0 = tmap.m0, n0 = tmap.n0;
-    const int K = L.K;
 
     // Per-lane byte offsets for the direct loads (logical chunk folded in). Rows
     // past M read the padding rows every activation buffer carries (at least one
@@ -200,6 +210,10 @@ hipError_t gemm_bf16(const GemmLaunch& L, hipStream_t s) {
     int total = 0;
     for (int i = 0; i < LL.ngroups; ++i) total += tiles_m(LL.g[i].M) * tiles_n;
     if (total == 0) return hipSuccess;
+    if (L.epi == EPI_PARTIAL) {
+        if (LL.ngroups != 1 || L.ksplit < 1 || L.K % (BK * L.ksplit) != 0) return hipErrorInvalidValue;
+        total *= L.ksplit;
+    }
     dim3 grid(total), block(GEMM_WM * GEMM_WN * 64);
     switch (L.epi) {
         case EPI_STORE: hipLaunchKernelGGL((k_gemm_bf16<EPI_STORE, GEMM_WM, GEMM_WN>), grid, block, 0, s, LL); break;
@@ -212,6 +226,7 @@ hipError_t gemm_bf16(const GemmLaunch& L, hipStream_t s) {
         case EPI_QKV: hipLaunchKernelGGL((k_gemm_bf16<EPI_QKV, GEMM_WM, GEMM_WN>), grid, block, 0, s, LL); break;
         case EPI_SWIGLU: hipLaunchKernelGGL((k_gemm_bf16<EPI_SWIGLU, GEMM_WM, GEMM_WN>), grid, block, 0, s, LL); break;
         case EPI_GEGLU: hipLaunchKernelGGL((k_gemm_bf16<EPI_GEGLU, GEMM_WM, GEMM_WN>), grid, block, 0, s, LL); break;
+        case EPI_PARTIAL: hipLaunchKernelGGL((k_gemm_bf16<EPI_PARTIAL, GEMM_WM, GEMM_WN>), grid, block, 0, s, LL); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -51,7 +51,7 @@ void k_gemm_mxfp8(GemmLaunch L) {
 
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WN, wn = wave % WN;
-    const TileMap tmap = tile_map(L);
+    const TileMap tmap = tile_map(L, blockIdx.x);
     const int gi = tmap.gi;
     const uint8_t* __restrict__ A = (const uint8_t*)(gi ? L.g[1].A : L.g[0].A);
     const long lda = gi ? L.g[1].lda : L.g[0].lda;      // bytes per row

@@ -69,13 +69,15 @@ struct TileMap {
     int gi, m0, n0, M, row0, gate_off;
 };
 
-__device__ __forceinline__ TileMap tile_map(const GemmLaunch& L) {
+// `b` is the workgroup's index among the launch's tiles (blockIdx.x, or its
+// remainder modulo the tile count when a launch repeats the tiles for K ranges).
+__device__ __forceinline__ TileMap tile_map(const GemmLaunch& L, int b) {
     const int tiles_n = L.N / BN;
     const int tm0 = tiles_m(L.g[0].M), tm1 = L.ngroups > 1 ? tiles_m(L.g[1].M) : 0;
     const int T0 = tm0 * tiles_n, T = T0 + tm1 * tiles_n;
     int lid;
     {
-        const int b = blockIdx.x, x = b % NXCD, q = T / NXCD, r = T % NXCD;
+        const int x = b % NXCD, q = T / NXCD, r = T % NXCD;
         lid = x * q + min(x, r) + b / NXCD;
     }
     const int gi = lid >= T0 ? 1 : 0;
@@ -116,7 +118,19 @@ __device__ __forceinline__ void epilogue(const GemmLaunch& L, f32x16 (&acc)[BM /
     const int rr_row = wm * TM + (lane & 31);           // row-major: row of mt = 0
     const int rr_col = wn * TN + (lane >> 5) * 4;       // row-major: column of nt = i = j = 0
 
-    if constexpr (EPI == EPI_STORE) {
+    if constexpr (EPI == EPI_PARTIAL) {
+        // fp32 partial sums, split slab selected through row0 = split * M
+        float* C = (float*)L.C;
+#pragma unroll 1
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                int m = m0 + lr_base + mt * 32 + (r >> 2) * 8 + (r & 3);
+                if (m >= M) continue;
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) C[(long)(row0 + m) * L.N + n0 + lc_base + nt * 32] = acc[mt][nt][r];
+            }
+    } else if constexpr (EPI == EPI_STORE) {
         bf16_t* C = (bf16_t*)L.C;
 #pragma unroll 1
         for (int mt = 0; mt < MT; ++mt)

@@ -777,3 +777,37 @@ hipError_t swiglu_f32(const float* raw, int M, int F, float* h, hipStream_t s) {
 }
 
 }  // namespace af
+
+namespace af {
+
+// ============================================================================ split-K sum
+// resid[i] += part[0][i] + part[1][i] + ... + part[ks - 1][i], added in that order
+// (deterministic); four consecutive values per thread.
+__global__ void k_splitk_resid(const float* __restrict__ part, int ks, long n, float* __restrict__ resid) {
+    const long i = ((long)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+    if (i >= n) return;
+    float4 acc = *reinterpret_cast<const float4*>(part + i);
+    for (int s = 1; s < ks; ++s) {
+        const float4 p = *reinterpret_cast<const float4*>(part + (long)s * n + i);
+        acc.x += p.x;
+        acc.y += p.y;
+        acc.z += p.z;
+        acc.w += p.w;
+    }
+    float4 r = *reinterpret_cast<const float4*>(resid + i);
+    r.x += acc.x;
+    r.y += acc.y;
+    r.z += acc.z;
+    r.w += acc.w;
+    *reinterpret_cast<float4*>(resid + i) = r;
+}
+
+hipError_t splitk_resid(const float* part, int ks, long M, int N, float* resid, hipStream_t s) {
+    const long n = M * N;
+    if (n == 0) return hipSuccess;
+    if (N % 4 != 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_splitk_resid, dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0, s, part, ks, n, resid);
+    return hipGetLastError();
+}
+
+}  // namespace af

@@ -87,6 +87,8 @@ struct af_umt5 {
     bf16_t* hbuf = nullptr;      // gated FFN output [Mp, d_ff]
     float* ones = nullptr;       // unit gate [d]
     float* bias_rows = nullptr;  // [L][H][2 Tmax - 1]
+    float* part = nullptr;       // split-K partial sums [KSPLIT_MAX][Mmax, d]
+    int n_cu = 0;
     float* staging = nullptr;
     size_t staging_floats = 0;
     void* work = nullptr;
@@ -182,11 +184,36 @@ GemmLaunch gemm_launch(const af_umt5* m, const void* A, long lda, const void* W,
     return L;
 }
 
+constexpr int KSPLIT_MAX = 4;
+
 #define U_K(call)                                                                                           \
     do {                                                                                                    \
         hipError_t e_ = (call);                                                                             \
         if (e_ != hipSuccess) return af::report(AF_E_HIP, (std::string(#call) + ": " + hipGetErrorString(e_)).c_str()); \
     } while (0)
+
+// x += A W^T for the N = d_model products (out-projection, FFN output). With few
+// 256 x 256 tiles for the compute units (M = B T rows is small for a text
+// encoder) and a long K (the FFN output, K = d_ff), K is cut into up to four
+// ranges whose fp32 partial sums are added to x in a fixed order afterwards.
+af_status resid_gemm(af_umt5* m, const void* A, long lda, const void* W, int K, int B, int T, hipStream_t s) {
+    const int d = m->cfg.d_model, M = B * T;
+    const int tiles = ((M + 255) / 256) * (d / 256);
+    // each range keeps at least 1280 of K: below that the fixed cost of a tile (pipeline
+    // fill, the fp32 partial store) and the extra summing pass outweigh the better fill
+    int ks = std::min({KSPLIT_MAX, m->n_cu / std::max(tiles, 1), K / 1280});
+    while (ks > 1 && K % (32 * ks) != 0) --ks;
+    if (ks < 2) {
+        U_K(gemm_bf16(gemm_launch(m, A, lda, W, lda, M, d, K, EPI_GATED_RESID, B, T), s));
+        return AF_OK;
+    }
+    GemmLaunch L = gemm_launch(m, A, lda, W, lda, M, d, K, EPI_PARTIAL, B, T);
+    L.C = m->part;
+    L.ksplit = ks;
+    U_K(gemm_bf16(L, s));
+    U_K(splitk_resid(m->part, ks, M, d, m->x, s));
+    return AF_OK;
+}
 
 af_status run_encode(af_umt5* m, const int32_t* ids, const uint8_t* mask, int B, int T, int stop_after, float* out,
                      hipStream_t s) {
@@ -208,13 +235,19 @@ af_status run_encode(af_umt5* m, const int32_t* ids, const uint8_t* mask, int B,
         Lq.ldc = 3 * d;
         U_K(gemm_bf16(Lq, s));
         U_K(umt5_attention(m->qkv, B, T, H, d, m->bias_rows + (size_t)l * H * (2 * T - 1), mask, m->attn, s));
-        U_K(gemm_bf16(gemm_launch(m, m->attn, d, buf(Ly.wo), d, M, d, d, EPI_GATED_RESID, B, T), s));
+        {
+            af_status st = resid_gemm(m, m->attn, d, buf(Ly.wo), d, B, T, s);
+            if (st != AF_OK) return st;
+        }
         U_K(umt5_rms_norm(m->x, M, d, (const float*)buf(Ly.ln2), c.eps, m->nrm, true, s));
         GemmLaunch Lf = gemm_launch(m, m->nrm, d, buf(Ly.wi01), d, M, 2 * F, d, EPI_GEGLU, B, T);
         Lf.C = m->hbuf;
         Lf.ldc = F;
         U_K(gemm_bf16(Lf, s));
-        U_K(gemm_bf16(gemm_launch(m, m->hbuf, F, buf(Ly.wo_ff), F, M, d, F, EPI_GATED_RESID, B, T), s));
+        {
+            af_status st = resid_gemm(m, m->hbuf, F, buf(Ly.wo_ff), F, B, T, s);
+            if (st != AF_OK) return st;
+        }
         if (stop_after == l) {
             U_HIP(hipMemcpyAsync(out, m->x, (size_t)M * d * 4, hipMemcpyDeviceToDevice, s));
             return AF_OK;
@@ -324,8 +357,11 @@ af_status af_umt5_create(const af_umt5_config* c, int device, af_umt5** out) {
         {(void**)&m->hbuf, (size_t)m->Mp * F * 2},
         {(void**)&m->ones, (size_t)d * 4},
         {(void**)&m->bias_rows, (size_t)std::max(c->num_layers, 1) * H * (2 * Tm - 1) * 4},
+        {(void**)&m->part, (size_t)KSPLIT_MAX * m->Mmax * d * 4},
         {(void**)&m->staging, m->staging_floats * 4},
     };
+    if (hipDeviceGetAttribute(&m->n_cu, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || m->n_cu <= 0)
+        return cleanup(AF_E_HIP, "compute-unit count query failed");
     size_t wtotal = 0;
     for (auto& e : ws) wtotal += align256(e.second);
     if (hipMalloc(&m->work, wtotal) != hipSuccess) return cleanup(AF_E_OOM, "workspace allocation failed");
