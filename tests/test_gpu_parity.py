@@ -181,6 +181,21 @@ def test_small_bf16_single_sample_odd_rows(af, small_bf16):
     assert e <= BF16_TOL and c >= BF16_COS, (e, c)
 
 
+def test_small_bf16_no_text(af, small_bf16):
+    """No text tokens (T = 0): the caption projection is skipped and attention runs over
+    the 8 registers and the image tokens only."""
+    torch = _torch()
+    cfg, m, _, _, _, _ = small_bf16
+    ocfg = oracle_cfg(cfg)
+    W_o = oracle.Weights.seeded(ocfg, seed=0, bf16=True)
+    lat, taus, text, mask = workload_inputs(2, 4, 18, 26, 0, 128, lengths=None, cfg_pairs=False)
+    ref = oracle.forward(ocfg, W_o, lat, taus, text, None, np.float32)
+    out = m.forward(to_dev(lat), to_dev(taus), to_dev(text), None).cpu().numpy()
+    torch.cuda.synchronize()
+    e, c = rel_max(out, ref), cosine(out, ref)
+    assert e <= BF16_TOL and c >= BF16_COS, (e, c)
+
+
 def test_small_bf16_deterministic_and_mask_invariant(af, small_bf16):
     torch = _torch()
     cfg, m, dev, ref, taps, host = small_bf16
