@@ -148,3 +148,37 @@ def test_full_1024_mxfp8_first_joint_and_single_blocks(af):
     e_plain = rel_max(got[4], plain4)
     print(f"block 4 against the oracle without MXFP8: rel {e_plain:.3e} cos {cosine(got[4], plain4):.6f}")
     assert e_plain > rel_max(got[4], x)
+
+
+def test_block_pair_mxfp8_non_square_latent(af):
+    """MXFP8 at the full width with a non-square latent and odd crop margins (66 x 158:
+    33 x 79 patches, S = 8 + 256 + 2607 = 2871 tokens per sample): ragged GEMM row tiles
+    and MXFP8 scale rows past the last real row."""
+    torch = _torch()
+    cfg = af.make_config(compute_dtype=af.AF_MXFP8, num_mmdit_layers=1, num_single_dit_layers=1, max_batch=2,
+                         max_latent_h=66, max_latent_w=158, max_text_len=256)
+    m = af.AuraFlowModel(cfg)
+    m.load_seeded_weights(seed=0, threads=16)
+    ocfg = oracle_cfg(cfg)
+    names = [n for n, _, _ in oracle.weight_specs(ocfg)]
+    Wseed = oracle.Weights.seeded(ocfg, seed=0, bf16=True)
+    W_o = oracle.Weights.from_dict(ocfg, {n: Wseed[n] for n in names})
+    lengths = seeded_inputs.valid_lengths(2, 16, 256)
+    lat, taus, text, mask = workload_inputs(2, 4, 66, 158, 256, 2048, lengths=lengths, cfg_pairs=True)
+    text = oracle.round_bf16(text)
+    dev = (to_dev(lat), to_dev(taus), to_dev(text), to_dev(mask))
+    got = {b: m.forward_taps(*dev, stop_after_block=b).cpu().numpy() for b in (0, 1)}
+    out = m.forward(*dev).cpu().numpy()
+    torch.cuda.synchronize()
+    m.close()
+    assert np.isfinite(out).all()
+    taps = {}
+    ref = oracle.forward(ocfg, W_o, lat, taus, text, mask, np.float32, mx=True,
+                         taps=lambda i, xt, xi: taps.__setitem__(i, np.concatenate([xt, xi], axis=1)))
+    for b in (0, 1):
+        e, c = rel_max(got[b], taps[b]), cosine(got[b], taps[b])
+        print(f"block {b}: rel {e:.3e} cos {c:.6f}")
+        assert e <= TOL and c >= COS, (b, e, c)
+    e, c = rel_max(out, ref), cosine(out, ref)
+    print(f"output: rel {e:.3e} cos {c:.6f}")
+    assert e <= TOL and c >= COS, (e, c)
