@@ -196,6 +196,24 @@ def test_small_bf16_no_text(af, small_bf16):
     assert e <= BF16_TOL and c >= BF16_COS, (e, c)
 
 
+def test_small_bf16_fully_padded_text_and_empty_batch(af, small_bf16):
+    """A sample whose text is all padding (only registers and image tokens are keys),
+    beside one with 7 valid tokens; and an empty batch, which enqueues nothing."""
+    torch = _torch()
+    cfg, m, _, _, _, _ = small_bf16
+    ocfg = oracle_cfg(cfg)
+    W_o = oracle.Weights.seeded(ocfg, seed=0, bf16=True)
+    lat, taus, text, mask = workload_inputs(2, 4, 22, 30, 13, 128, lengths=[0, 7], cfg_pairs=False)
+    text = oracle.round_bf16(text)
+    ref = oracle.forward(ocfg, W_o, lat, taus, text, mask, np.float32)
+    out = m.forward(to_dev(lat), to_dev(taus), to_dev(text), to_dev(mask)).cpu().numpy()
+    e, c = rel_max(out, ref), cosine(out, ref)
+    assert e <= BF16_TOL and c >= BF16_COS, (e, c)
+    empty = m.forward(to_dev(lat[:0]), to_dev(taus[:0]), to_dev(text[:0]), to_dev(mask[:0]))
+    torch.cuda.synchronize()
+    assert tuple(empty.shape) == (0, 4, 22, 30)
+
+
 def test_small_bf16_deterministic_and_mask_invariant(af, small_bf16):
     torch = _torch()
     cfg, m, dev, ref, taps, host = small_bf16

@@ -127,3 +127,13 @@ def test_full_width_two_layers(af):
         _check(m, U.UMT5_PAIR, ids, mask, [0, 1])
     finally:
         m.close()
+
+
+def test_small_empty_batch_and_no_tokens(af, small):
+    """B = 0 or T = 0 enqueue nothing and return an empty result."""
+    torch = _torch()
+    ids = torch.zeros((0, 5), dtype=torch.int32, device="cuda")
+    assert tuple(small.encode(ids).shape) == (0, 5, U.UMT5_SMALL.d_model)
+    ids = torch.zeros((2, 0), dtype=torch.int32, device="cuda")
+    assert tuple(small.encode(ids).shape) == (2, 0, U.UMT5_SMALL.d_model)
+    torch.cuda.synchronize()
