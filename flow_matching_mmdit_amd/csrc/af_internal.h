@@ -47,6 +47,7 @@ struct GemmLaunch {
     float eps;
     float q_scale;                     // QKV: factor on the normalised q before rounding (1 = none)
     int ksplit;                        // PARTIAL: number of K ranges (K a multiple of 32 ksplit)
+    int n_cu;                          // compute units (0: always 256 x 256 tiles); N a multiple of 256
 };
 
 hipError_t gemm_bf16(const GemmLaunch& L, hipStream_t s);

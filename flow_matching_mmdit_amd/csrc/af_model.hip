@@ -402,6 +402,7 @@ GemmLaunch gemm_base(af_model* m, const float* mod, RowGeom g, int N, int K, int
     L.hd = m->D.hd;
     L.eps = m->cfg.ln_eps;
     L.q_scale = 1.f;
+    L.n_cu = m->n_cu;   // lets small launches use 128 x 128 tiles
     return L;
 }
 

@@ -37,14 +37,21 @@ namespace af {
 
 using namespace gemm;
 
-// WM x WN waves; each wave owns a (256 / WM) x (256 / WN) sub-tile.
-template <int EPI, int WM, int WN>
-__global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4)))
+// BM_ x BN_ block tile (square: A and W sub-tiles share one layout), WM x WN
+// waves, each owning a (BM_ / WM) x (BN_ / WN) sub-tile. 256 x 256 with 8 waves is
+// the main configuration (one workgroup per CU); 128 x 128 with 4 waves (two
+// workgroups per CU) serves launches with too few 256 x 256 tiles to fill the GPU.
+template <int EPI, int WM, int WN, int BM_ = BM, int BN_ = BN>
+__global__ __launch_bounds__(WM * WN * 64)
+__attribute__((amdgpu_waves_per_eu(BM_ == 256 ? WM * WN / 4 : 2, BM_ == 256 ? WM * WN / 4 : 2)))
 void k_gemm_bf16(GemmLaunch L) {
     constexpr int NW = WM * WN, NTHR = NW * 64;
-    constexpr int TM = BM / WM, TN = BN / WN, MT = TM / 32, NT = TN / 32;
-    static_assert(((BM / RPI) / NW) % 2 == 0, "per-wave load count must be even");
-    __shared__ __attribute__((aligned(1024))) bf16_t smem[SMEM_ELEMS];
+    constexpr int TM = BM_ / WM, TN = BN_ / WN, MT = TM / 32, NT = TN / 32;
+    constexpr int TILE = BM_ * BK;   // bf16 elements of one staged A (or W) sub-tile
+    static_assert(BM_ == BN_, "A and W sub-tiles share one layout");
+    static_assert(((BM_ / RPI) / NW) % 2 == 0, "per-wave load count must be even");
+    static_assert(BM_ == 256 || 2 * NS * TILE >= BM_ * HS, "the gated epilogue's staging fits the operand slots");
+    __shared__ __attribute__((aligned(1024))) bf16_t smem[BM_ == 256 ? SMEM_ELEMS : 2 * NS * TILE];
 
     // wave index in a scalar register: the LDS addresses of the direct loads (M0)
     // are then formed with scalar arithmetic
@@ -54,11 +61,11 @@ void k_gemm_bf16(GemmLaunch L) {
     // PARTIAL: the launch repeats the tile set once per K range
     int bid = blockIdx.x, split = 0;
     if constexpr (EPI == EPI_PARTIAL) {
-        const int T = tiles_m(L.g[0].M) * (L.N / BN);
+        const int T = tiles_m<BM_>(L.g[0].M) * (L.N / BN_);
         split = bid / T;
         bid -= split * T;
     }
-    const TileMap tmap = tile_map(L, bid);
+    const TileMap tmap = tile_map<BM_, BN_>(L, bid);
     const int gi = tmap.gi;
     const long lda = gi ? L.g[1].lda : L.g[0].lda;
     const long ldw = gi ? L.g[1].ldw : L.g[0].ldw;
@@ -75,7 +82,7 @@ void k_gemm_bf16(GemmLaunch L) {
     uint32_t aoff[2], woff[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-        const int r = (wave * ((BM / RPI) / NW) + j) * RPI + lane / CH;
+        const int r = (wave * ((BM_ / RPI) / NW) + j) * RPI + lane / CH;
         const int c = (lane % CH) ^ swz(r);
         aoff[j] = (uint32_t)((r * lda + c * 8) * 2);
         woff[j] = (uint32_t)((r * ldw + c * 8) * 2);
@@ -119,7 +126,7 @@ void k_gemm_bf16(GemmLaunch L) {
     // Issue order inside a k-step: the fragment reads for the next k-step, then
     // the MFMAs with the k-step's direct loads slotted in after the first and the
     // third MFMA.
-    static_assert(MT * NT == 8 && (BM / RPI) / NW == 2, "issue pattern is laid out for the 4 x 2 wave grid");
+    static_assert(MT * NT >= 4 && (BM_ / RPI) / NW == 2, "issue pattern: two direct loads among >= 4 MFMAs");
     auto pattern = []() {
         __builtin_amdgcn_sched_group_barrier(0x100, MT + NT, 0);   // DS reads
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);         // MFMA
@@ -138,16 +145,16 @@ void k_gemm_bf16(GemmLaunch L) {
     //             j + 1's k-step 0; MFMAs of k-step 1.
     // Loads past the last sub-tile re-read the last one into a free slot, so the
     // loop body has no branches and the wait counts are the same every iteration.
-    constexpr int PER = (BM / RPI) / NW;     // direct loads per wave per operand per sub-tile
+    constexpr int PER = (BM_ / RPI) / NW;    // direct loads per wave per operand per sub-tile
     constexpr int PER2 = 2 * PER;
     const int KT = K / BK;
-    auto slot_ptr = [&](int st) { return smem + st * 2 * TILE_ELEMS; };
+    auto slot_ptr = [&](int st) { return smem + st * 2 * TILE; };
     const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc((void*)Atile, (short)0, 0x7fffffff, 0x00020000);
     const __amdgpu_buffer_rsrc_t rW = __builtin_amdgcn_make_buffer_rsrc((void*)Wtile, (short)0, 0x7fffffff, 0x00020000);
     const int ldab = (int)lda * 2, ldwb = (int)ldw * 2;
-    auto issueA = [&](int t, int st) { issue_tile<NW>(rA, aoff, min(t, KT - 1) * BK * 2, ldab, slot_ptr(st), wave); };
+    auto issueA = [&](int t, int st) { issue_tile<NW, BM_>(rA, aoff, min(t, KT - 1) * BK * 2, ldab, slot_ptr(st), wave); };
     auto issueW = [&](int t, int st) {
-        issue_tile<NW>(rW, woff, min(t, KT - 1) * BK * 2, ldwb, slot_ptr(st) + TILE_ELEMS, wave);
+        issue_tile<NW, BN_>(rW, woff, min(t, KT - 1) * BK * 2, ldwb, slot_ptr(st) + TILE, wave);
     };
     auto mainloop = [&](auto orient) {
     #pragma unroll
@@ -159,7 +166,7 @@ void k_gemm_bf16(GemmLaunch L) {
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER2 * (NS - 3) + PER));   // sub-tile 0 landed
         __builtin_amdgcn_s_barrier();
         bf16x8 fa0[MT], fb0[NT], fa1[MT], fb1[NT];
-        load_frags(slot_ptr(0), slot_ptr(0) + TILE_ELEMS, 0, fa0, fb0);
+        load_frags(slot_ptr(0), slot_ptr(0) + TILE, 0, fa0, fb0);
         int cs = 0;
         for (int j = 0; j < KT; ++j) {
             const bf16_t* cur = slot_ptr(cs);
@@ -167,7 +174,7 @@ void k_gemm_bf16(GemmLaunch L) {
             const int fs = cs == 0 ? NS - 1 : cs - 1;      // slot of j - 1
             const int f2 = fs == 0 ? NS - 1 : fs - 1;      // slot of j - 2
             issueW(j + NS - 2, f2);
-            load_frags(cur, cur + TILE_ELEMS, 1, fa1, fb1);
+            load_frags(cur, cur + TILE, 1, fa1, fb1);
             mfmas(fa0, fb0, orient);
             pattern();
             __builtin_amdgcn_sched_barrier(0);
@@ -176,7 +183,7 @@ void k_gemm_bf16(GemmLaunch L) {
             __builtin_amdgcn_sched_barrier(0);
             issueA(j + NS - 1, fs);
             const bf16_t* nxt = slot_ptr(ns);
-            load_frags(nxt, nxt + TILE_ELEMS, 0, fa0, fb0);
+            load_frags(nxt, nxt + TILE, 0, fa0, fb0);
             mfmas(fa1, fb1, orient);
             pattern();
             __builtin_amdgcn_sched_barrier(0);
@@ -196,11 +203,10 @@ void k_gemm_bf16(GemmLaunch L) {
         mainloop(Orient<false>{});
     }
 
-    epilogue<EPI, WM, WN, false>(L, acc, smem, tid, lane, wm, wn, m0, n0, M, row0, gate_off);
+    epilogue<EPI, WM, WN, false, BM_, BN_>(L, acc, smem, tid, lane, wm, wn, m0, n0, M, row0, gate_off);
 }
 
 hipError_t gemm_bf16(const GemmLaunch& L, hipStream_t s) {
-    int tiles_n = L.N / BN;
     GemmLaunch LL = L;
     if (LL.ngroups == 2 && LL.g[0].M == 0) {  // keep group 0 non-empty
         LL.g[0] = LL.g[1];
@@ -208,12 +214,32 @@ hipError_t gemm_bf16(const GemmLaunch& L, hipStream_t s) {
     }
     if (LL.ngroups == 2 && LL.g[1].M == 0) LL.ngroups = 1;
     int total = 0;
-    for (int i = 0; i < LL.ngroups; ++i) total += tiles_m(LL.g[i].M) * tiles_n;
+    for (int i = 0; i < LL.ngroups; ++i) total += tiles_m(LL.g[i].M) * (L.N / BN);
     if (total == 0) return hipSuccess;
-    if (L.epi == EPI_PARTIAL) {
-        if (LL.ngroups != 1 || L.ksplit < 1 || L.K % (BK * L.ksplit) != 0) return hipErrorInvalidValue;
-        total *= L.ksplit;
+    if (L.epi == EPI_PARTIAL && (LL.ngroups != 1 || L.ksplit < 1 || L.K % (BK * L.ksplit) != 0))
+        return hipErrorInvalidValue;
+    const int ks = L.epi == EPI_PARTIAL ? L.ksplit : 1;
+    // 128 x 128 tiles (two workgroups per CU) when the 256 x 256 tiles, K ranges
+    // included, would occupy at most half of the compute units: one round of the
+    // small tiles then takes about half the time of the large tiles' round
+    const bool small = L.n_cu > 0 && 2 * total * ks <= L.n_cu && L.epi != EPI_QKV && L.epi != EPI_STORE_MAPPED;
+    if (small) {
+        int t128 = 0;
+        for (int i = 0; i < LL.ngroups; ++i) t128 += tiles_m<128>(LL.g[i].M) * (L.N / 128);
+        const dim3 grid(t128 * ks), block(4 * 64);
+#define AF_G128(E) hipLaunchKernelGGL((k_gemm_bf16<E, 2, 2, 128, 128>), grid, block, 0, s, LL)
+        switch (L.epi) {
+            case EPI_STORE: AF_G128(EPI_STORE); break;
+            case EPI_GATED_RESID: AF_G128(EPI_GATED_RESID); break;
+            case EPI_SWIGLU: AF_G128(EPI_SWIGLU); break;
+            case EPI_GEGLU: AF_G128(EPI_GEGLU); break;
+            case EPI_PARTIAL: AF_G128(EPI_PARTIAL); break;
+            default: return hipErrorInvalidValue;
+        }
+#undef AF_G128
+        return hipGetLastError();
     }
+    total *= ks;
     dim3 grid(total), block(GEMM_WM * GEMM_WN * 64);
     switch (L.epi) {
         case EPI_STORE: hipLaunchKernelGGL((k_gemm_bf16<EPI_STORE, GEMM_WM, GEMM_WN>), grid, block, 0, s, LL); break;

@@ -39,7 +39,8 @@ __device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
 // s_waitcnt immediate that waits until at most n vector-memory operations are
 // outstanding (expcnt and lgkmcnt left unconstrained).
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
-__host__ __device__ __forceinline__ int tiles_m(int M) { return (M + BM - 1) / BM; }
+template <int BM_ = BM>
+__host__ __device__ __forceinline__ int tiles_m(int M) { return (M + BM_ - 1) / BM_; }
 // MFMA operand order of a tile: false -> acc = A W^T (a lane holds one column and
 // four consecutive rows per 4-register group), true -> acc = (W A^T) = C^T (a lane
 // holds one row and four consecutive columns), for epilogues that reduce or store
@@ -53,10 +54,10 @@ template <bool T> struct Orient { static constexpr bool value = T; };
 // its 16-row block, so per-lane byte offsets for two blocks (voff[j & 1]) plus a
 // uniform row step (in the scalar offset, with the sub-tile's k offset `sbase`)
 // cover all of the wave's instructions.
-template <int NW>
+template <int NW, int ROWS = BM>
 __device__ __forceinline__ void issue_tile(__amdgpu_buffer_rsrc_t rsrc, const uint32_t* voff, int sbase, int ldbytes,
                                            bf16_t* lds_tile, int wave) {
-    constexpr int PER = (BM / RPI) / NW;
+    constexpr int PER = (ROWS / RPI) / NW;
 #pragma unroll
     for (int j = 0; j < PER; ++j)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(lds_tile + (wave * PER + j) * 512), 16, voff[j & 1],
@@ -71,9 +72,10 @@ struct TileMap {
 
 // `b` is the workgroup's index among the launch's tiles (blockIdx.x, or its
 // remainder modulo the tile count when a launch repeats the tiles for K ranges).
+template <int BM_ = BM, int BN_ = BN>
 __device__ __forceinline__ TileMap tile_map(const GemmLaunch& L, int b) {
-    const int tiles_n = L.N / BN;
-    const int tm0 = tiles_m(L.g[0].M), tm1 = L.ngroups > 1 ? tiles_m(L.g[1].M) : 0;
+    const int tiles_n = L.N / BN_;
+    const int tm0 = tiles_m<BM_>(L.g[0].M), tm1 = L.ngroups > 1 ? tiles_m<BM_>(L.g[1].M) : 0;
     const int T0 = tm0 * tiles_n, T = T0 + tm1 * tiles_n;
     int lid;
     {
@@ -93,8 +95,8 @@ __device__ __forceinline__ TileMap tile_map(const GemmLaunch& L, int b) {
     }
     TileMap t;
     t.gi = gi;
-    t.m0 = tm * BM;
-    t.n0 = tn * BN;
+    t.m0 = tm * BM_;
+    t.n0 = tn * BN_;
     t.M = gi ? L.g[1].M : L.g[0].M;
     t.row0 = gi ? L.g[1].row0 : L.g[0].row0;
     t.gate_off = gi ? L.g[1].gate_off : L.g[0].gate_off;
@@ -103,12 +105,12 @@ __device__ __forceinline__ TileMap tile_map(const GemmLaunch& L, int b) {
 
 // Fused epilogues on the fp32 accumulators of a 256 x 256 tile. MXOUT: the
 // SwiGLU output is MXFP8 (fp8 values + block scales) instead of bf16.
-template <int EPI, int WM, int WN, bool MXOUT>
-__device__ __forceinline__ void epilogue(const GemmLaunch& L, f32x16 (&acc)[BM / WM / 32][BN / WN / 32], bf16_t* smem,
+template <int EPI, int WM, int WN, bool MXOUT, int BM_ = BM, int BN_ = BN>
+__device__ __forceinline__ void epilogue(const GemmLaunch& L, f32x16 (&acc)[BM_ / WM / 32][BN_ / WN / 32], bf16_t* smem,
                                          int tid, int lane, int wm, int wn, int m0, int n0, int M, int row0,
                                          int gate_off) {
     constexpr int NW = WM * WN, NTHR = NW * 64;
-    constexpr int TM = BM / WM, TN = BN / WN, MT = TM / 32, NT = TN / 32;
+    constexpr int TM = BM_ / WM, TN = BN_ / WN, MT = TM / 32, NT = TN / 32;
     // Column-major orientation: acc[mt][nt][i*4+j] holds row wm*64 + mt*32 + i*8 +
     // (lane>>5)*4 + j, column wn*128 + nt*32 + (lane&31) of the block tile.
     // Row-major orientation: acc[mt][nt][i*4+j] holds row wm*64 + mt*32 + (lane&31),
@@ -195,6 +197,7 @@ __device__ __forceinline__ void epilogue(const GemmLaunch& L, f32x16 (&acc)[BM /
             }
         }
     } else if constexpr (EPI == EPI_SWIGLU && MXOUT) {
+        static_assert(BM_ == 256 && BN_ == 256, "the MXFP8 SwiGLU epilogue is laid out for 256 x 256 tiles");
         // h = silu(gate) * up as MXFP8: every 32 h columns of a row share one
         // power-of-two scale 2^e, e = floor(log2(max |h|)) - 8 (at least -127);
         // elements h / 2^e clamped to +-448 and rounded to E4M3. Row-major
@@ -264,10 +267,11 @@ __device__ __forceinline__ void epilogue(const GemmLaunch& L, f32x16 (&acc)[BM /
         __syncthreads();
         bf16_t* Hout = (bf16_t*)L.C;
         const int fcol0 = n0 / 2;
+        constexpr int CPR = BN_ / 16;          // 16-byte chunks of h per tile row
 #pragma unroll 4
-        for (int it = 0; it < 4096 / NTHR; ++it) {
-            int idx = it * NTHR + tid;         // 256 rows x 16 chunks
-            int lr = idx >> 4, ch = idx & 15;
+        for (int it = 0; it < BM_ * CPR / NTHR; ++it) {
+            int idx = it * NTHR + tid;         // BM_ rows x CPR chunks
+            int lr = idx / CPR, ch = idx % CPR;
             int m = m0 + lr;
             if (m < M) {
                 uint4 v = *reinterpret_cast<const uint4*>(st + lr * HS + ch * 8);
@@ -275,6 +279,7 @@ __device__ __forceinline__ void epilogue(const GemmLaunch& L, f32x16 (&acc)[BM /
             }
         }
     } else if constexpr (EPI == EPI_QKV) {
+        static_assert(BM_ == 256 && BN_ == 256, "one QKV tile is one 256-wide head");
         const int dmodel = L.N / 3;
         const int which = n0 / dmodel;          // 0 q, 1 k, 2 v
         const int head = (n0 % dmodel) / BN;    // one block tile = one 256-wide head

@@ -181,6 +181,7 @@ GemmLaunch gemm_launch(const af_umt5* m, const void* A, long lda, const void* W,
     L.mod = m->ones;        // unit gate: resid += acc
     L.mod_stride = 0;
     L.geom = RowGeom{B, T, 0};
+    L.n_cu = m->n_cu;   // lets small launches use 128 x 128 tiles
     return L;
 }
 
@@ -200,8 +201,10 @@ af_status resid_gemm(af_umt5* m, const void* A, long lda, const void* W, int K, 
     const int d = m->cfg.d_model, M = B * T;
     const int tiles = ((M + 255) / 256) * (d / 256);
     // each range keeps at least 1280 of K: below that the fixed cost of a tile (pipeline
-    // fill, the fp32 partial store) and the extra summing pass outweigh the better fill
-    int ks = std::min({KSPLIT_MAX, m->n_cu / std::max(tiles, 1), K / 1280});
+    // fill, the fp32 partial store) and the extra summing pass outweigh the better fill.
+    // Ranges are counted against two 128 x 128-tile workgroups per CU (gemm_bf16 takes
+    // that tile size when the 256 x 256 tiles fill at most half the CUs).
+    int ks = std::min({KSPLIT_MAX, m->n_cu / std::max(2 * tiles, 1), K / 1280});
     while (ks > 1 && K % (32 * ks) != 0) --ks;
     if (ks < 2) {
         U_K(gemm_bf16(gemm_launch(m, A, lda, W, lda, M, d, K, EPI_GATED_RESID, B, T), s));
