@@ -272,6 +272,8 @@ def main():
                     help="time only the text encoder (8 prompts x 256 tokens) and print its own line")
     ap.add_argument("--no-text-encoder-leg", action="store_true",
                     help="skip the text-encoder timing reported beside the transformer line")
+    ap.add_argument("--no-graph-leg", action="store_true",
+                    help="skip the graph-replay timing reported beside the eager line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run the plain 512 MiB device copy used to scale the HBM byte counters")
     args = ap.parse_args()
@@ -371,6 +373,35 @@ def main():
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     check_finite("the timed forwards")
     print(f"[bench] {ms_per_step:.2f} ms/forward, {tflops:.1f} TFLOP/s", file=sys.stderr, flush=True)
+
+    # The same forward captured once in a HIP graph (through torch's capture of the
+    # current stream) and replayed: no host launch work inside the timed region.
+    graph_leg = None
+    if not args.no_graph_leg:
+        out_g = torch.empty_like(out)
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            model.forward(lat, tau, text, mask, out=out_g)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            model.forward(lat, tau, text, mask, out=out_g)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_g, out), "graph replay differs from the eager forward"
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.steps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        msg = e0.elapsed_time(e1) / args.steps
+        graph_leg = {"ms_per_step": msg, "value": 1000.0 / msg, "unit": "forwards/s",
+                     "note": "the forward captured once in a HIP graph and replayed (same kernels, outputs equal)"}
+        del g
+        print(f"[bench] graph replay: {msg:.2f} ms/forward", file=sys.stderr, flush=True)
 
     kernels, roofline = {}, None
     if not args.no_profile:
@@ -474,6 +505,7 @@ def main():
         "forward_ms_percentiles": pct,
         "flops_per_forward": flops,
         "roofline": roofline,
+        "graph_replay": graph_leg,
         "mxfp8_model": mx_leg,
         "text_encoder": te,
         "cpu_baseline": cpu,
