@@ -92,6 +92,8 @@ af_status derive(const af_config* c, Derived* out) {
     if (c->compute_dtype != AF_F32) {
         if (d.hd != 256) return fail(AF_E_UNSUPPORTED, "bf16 path is built for attention_head_dim 256");
         if (d.d % 256 != 0) return fail(AF_E_UNSUPPORTED, "bf16 path needs inner dim % 256 == 0");
+        if (c->out_channels * c->patch_size * c->patch_size > 16)
+            return fail(AF_E_UNSUPPORTED, "bf16 path: output patch vectors longer than 16 are not built");
         if (c->joint_attention_dim % 64 != 0)
             return fail(AF_E_UNSUPPORTED, "bf16 path needs joint_attention_dim % 64 == 0");
     } else {

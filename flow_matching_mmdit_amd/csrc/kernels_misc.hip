@@ -6,6 +6,8 @@
 // Euler + CFG update, weight packing and fp32-path helpers.
 //
 // Page tags: [PIPE], [TRANS], [DEEP] as listed in include/auraflow.h.
+#include <algorithm>
+
 #include "af_internal.h"
 
 namespace af {
@@ -531,14 +533,78 @@ hipError_t ln_modulate_mx(const float* x, int M, int d, RowGeom g, int split, co
 // [TRANS] 核心子模块架构 (调制与归一化) and 前向传播流程: y = x (1 + scale) + shift
 // on the image rows (modulation only), z = y W_out^T (no bias), and z's
 // features (row-in-patch, column-in-patch, channel) scattered back to
-// [B, C_out, H, W]. One wave per image token; fp32 throughout.
-template <typename WT>
-__global__ __launch_bounds__(256) void k_prefinal_project(const float* __restrict__ resid, RowGeom g, int d,
-                                                          const float* __restrict__ mod, long mod_stride,
-                                                          int sc_off, int sh_off, const WT* __restrict__ Wout,
-                                                          int Cout, int p, int h, int w,
-                                                          float* __restrict__ out) {
-    constexpr int MAXV = 16;
+// [B, C_out, H, W]. fp32 arithmetic.
+//
+// bf16 weights: one workgroup of 8 waves per CU stages W_out (p^2 C_out <= 16 rows of
+// d <= 4096; 96 KB at d = 3072) in LDS once; each wave then takes image tokens in turn, holds the
+// modulated row in registers, accumulates all p^2 C_out dot products from 8-byte
+// LDS reads of W_out and reduces them across the wave independently of each other.
+constexpr int PF_MAXV = 16;
+constexpr int PF_MAXO = 16;
+constexpr int PF_LDS = 16 * 4096;   // bf16 elements of W_out the LDS stage holds (128 KB)
+
+template <int NV4>   // d = 256 NV4: every lane holds NV4 float4 of a row, no partial chunks
+__global__ __launch_bounds__(512) void k_prefinal_project_bf16(const float* __restrict__ resid, RowGeom g, int d,
+                                                               const float* __restrict__ mod, long mod_stride,
+                                                               int sc_off, int sh_off,
+                                                               const bf16_t* __restrict__ Wout, int Cout, int p,
+                                                               int h, int w, float* __restrict__ out) {
+    __shared__ __attribute__((aligned(16))) bf16_t sW[PF_LDS];
+    const int Pout = p * p * Cout;
+    for (int e = threadIdx.x * 8; e < Pout * d; e += blockDim.x * 8)
+        *reinterpret_cast<uint4*>(sW + e) = *reinterpret_cast<const uint4*>(Wout + e);
+    __syncthreads();
+    const int lane = threadIdx.x & 63;
+    const int wave = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+    const int nwaves = (gridDim.x * blockDim.x) >> 6;
+    const int ntok = g.B * g.Ni;
+    const int H = h * p, W = w * p;
+    for (int t = wave; t < ntok; t += nwaves) {
+        const int b = t / g.Ni, tok = t % g.Ni;
+        const float4* xr = reinterpret_cast<const float4*>(resid + (long)(g.B * g.Nt + t) * d);
+        const float4* sc = reinterpret_cast<const float4*>(mod + (long)b * mod_stride + sc_off);
+        const float4* sh = reinterpret_cast<const float4*>(mod + (long)b * mod_stride + sh_off);
+        float4 y[NV4];
+#pragma unroll
+        for (int i = 0; i < NV4; ++i) {
+            const int c4 = lane + 64 * i;
+            const float4 xv = xr[c4], s4 = sc[c4], h4 = sh[c4];
+            y[i] = make_float4(xv.x * (1.f + s4.x) + h4.x, xv.y * (1.f + s4.y) + h4.y,
+                               xv.z * (1.f + s4.z) + h4.z, xv.w * (1.f + s4.w) + h4.w);
+        }
+        float acc[PF_MAXO];
+#pragma unroll
+        for (int o = 0; o < PF_MAXO; ++o) {
+            float a = 0.f;
+            if (o < Pout) {   // wave-uniform
+#pragma unroll
+                for (int i = 0; i < NV4; ++i) {
+                    const uint2 wv = *reinterpret_cast<const uint2*>(sW + o * d + 4 * (lane + 64 * i));
+                    a += y[i].x * __uint_as_float(wv.x << 16) + y[i].y * __uint_as_float(wv.x & 0xffff0000u) +
+                         y[i].z * __uint_as_float(wv.y << 16) + y[i].w * __uint_as_float(wv.y & 0xffff0000u);
+                }
+            }
+            acc[o] = a;
+        }
+#pragma unroll
+        for (int o = 0; o < PF_MAXO; ++o) acc[o] = wave_sum(acc[o]);
+        const int ti = tok / w, tj = tok % w;
+        if (lane < Pout) {
+            float v = 0.f;
+#pragma unroll
+            for (int o = 0; o < PF_MAXO; ++o) v = lane == o ? acc[o] : v;
+            const int o = lane, py = o / (p * Cout), px = (o / Cout) % p, ch = o % Cout;
+            out[(((long)b * Cout + ch) * H + ti * p + py) * W + tj * p + px] = v;
+        }
+    }
+}
+
+// fp32 weights (the full-precision configuration, small widths): one wave per token.
+__global__ __launch_bounds__(256) void k_prefinal_project_f32(const float* __restrict__ resid, RowGeom g, int d,
+                                                              const float* __restrict__ mod, long mod_stride,
+                                                              int sc_off, int sh_off, const float* __restrict__ Wout,
+                                                              int Cout, int p, int h, int w,
+                                                              float* __restrict__ out) {
     constexpr int MAXO = 64;
     const int lane = threadIdx.x & 63;
     const int wave = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
@@ -551,9 +617,9 @@ __global__ __launch_bounds__(256) void k_prefinal_project(const float* __restric
         const float* xr = resid + (long)(g.B * g.Nt + t) * d;
         const float* sc = mod + (long)b * mod_stride + sc_off;
         const float* sh = mod + (long)b * mod_stride + sh_off;
-        float4 y[MAXV];
+        float4 y[PF_MAXV];
 #pragma unroll
-        for (int i = 0; i < MAXV; ++i) {
+        for (int i = 0; i < PF_MAXV; ++i) {
             int c4 = lane + 64 * i;
             if (c4 < nv) {
                 float4 xv = reinterpret_cast<const float4*>(xr)[c4];
@@ -568,15 +634,14 @@ __global__ __launch_bounds__(256) void k_prefinal_project(const float* __restric
         const int ti = tok / w, tj = tok % w;
         const int H = h * p, W = w * p;
         for (int o = 0; o < Pout && o < MAXO; ++o) {
-            const WT* wr = Wout + (long)o * d;
+            const float* wr = Wout + (long)o * d;
             float acc = 0.f;
 #pragma unroll
-            for (int i = 0; i < MAXV; ++i) {
+            for (int i = 0; i < PF_MAXV; ++i) {
                 int c4 = lane + 64 * i;
                 if (c4 < nv) {
-                    int c = 4 * c4;
-                    acc += y[i].x * WChunk<WT>::one(wr + c) + y[i].y * WChunk<WT>::one(wr + c + 1) +
-                           y[i].z * WChunk<WT>::one(wr + c + 2) + y[i].w * WChunk<WT>::one(wr + c + 3);
+                    const float4 wv = reinterpret_cast<const float4*>(wr)[c4];
+                    acc += y[i].x * wv.x + y[i].y * wv.y + y[i].z * wv.z + y[i].w * wv.w;
                 }
             }
             acc = wave_sum(acc);
@@ -591,16 +656,33 @@ __global__ __launch_bounds__(256) void k_prefinal_project(const float* __restric
 hipError_t prefinal_project(const float* resid, RowGeom g, int d, const float* mod, long mod_stride, int sc_off,
                             int sh_off, const void* Wout, af_dtype wdt, int Cout, int p, int h, int w,
                             float* out, hipStream_t s) {
-    int ntok = g.B * g.Ni;
+    const int ntok = g.B * g.Ni;
     if (ntok == 0) return hipSuccess;
-    int blocks = (ntok + 3) / 4;
-    if (blocks > 2048) blocks = 2048;
-    if (wdt == AF_BF16)
-        hipLaunchKernelGGL(k_prefinal_project<bf16_t>, dim3(blocks), dim3(256), 0, s, resid, g, d, mod,
-                           mod_stride, sc_off, sh_off, (const bf16_t*)Wout, Cout, p, h, w, out);
-    else
-        hipLaunchKernelGGL(k_prefinal_project<float>, dim3(blocks), dim3(256), 0, s, resid, g, d, mod,
-                           mod_stride, sc_off, sh_off, (const float*)Wout, Cout, p, h, w, out);
+    const int Pout = p * p * Cout;
+    if (wdt == AF_BF16) {
+        if (Pout > PF_MAXO || (long)Pout * d > PF_LDS || d % 256 != 0) return hipErrorInvalidValue;
+        int n_cu = 0, dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu <= 0)
+            n_cu = 256;
+        const int blocks = std::min(n_cu, (ntok + 7) / 8);   // one workgroup of 8 waves per CU
+#define AF_PF(V) hipLaunchKernelGGL(k_prefinal_project_bf16<V>, dim3(blocks), dim3(512), 0, s, resid, g, d, mod, \
+                                    mod_stride, sc_off, sh_off, (const bf16_t*)Wout, Cout, p, h, w, out)
+        switch (d / 256) {   // the bf16 path has d a multiple of 256, at most 4096
+            case 1: AF_PF(1); break;   case 2: AF_PF(2); break;   case 3: AF_PF(3); break;
+            case 4: AF_PF(4); break;   case 5: AF_PF(5); break;   case 6: AF_PF(6); break;
+            case 7: AF_PF(7); break;   case 8: AF_PF(8); break;   case 9: AF_PF(9); break;
+            case 10: AF_PF(10); break; case 11: AF_PF(11); break; case 12: AF_PF(12); break;
+            case 13: AF_PF(13); break; case 14: AF_PF(14); break; case 15: AF_PF(15); break;
+            case 16: AF_PF(16); break;
+            default: return hipErrorInvalidValue;
+        }
+#undef AF_PF
+    } else {
+        const int blocks = std::min(2048, (ntok + 3) / 4);
+        hipLaunchKernelGGL(k_prefinal_project_f32, dim3(blocks), dim3(256), 0, s, resid, g, d, mod, mod_stride,
+                           sc_off, sh_off, (const float*)Wout, Cout, p, h, w, out);
+    }
     return hipGetLastError();
 }
 
