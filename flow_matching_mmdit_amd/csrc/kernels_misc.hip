@@ -364,7 +364,10 @@ template <> __device__ __forceinline__ void store4<float>(float* p, float a, flo
     *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
 }
 
-template <typename OT, int MAXV>   // MAXV float4 per lane: d <= 256 MAXV
+// EXACT: d == 256 MAXV, every lane's MAXV chunks are in the row and the loops carry
+// no per-chunk condition (with one, each chunk's shift/scale loads and store sat in
+// a branch of its own behind a full wait: twelve serial L2 round trips per row).
+template <typename OT, int MAXV, bool EXACT = false>   // MAXV float4 per lane: d <= 256 MAXV
 __global__ __launch_bounds__(256) void k_ln_modulate(const float* __restrict__ x, int M, int d, RowGeom g,
                                                      int split, const float* __restrict__ mod,
                                                      long mod_stride, int sh_a, int sc_a, int sh_b,
@@ -372,7 +375,7 @@ __global__ __launch_bounds__(256) void k_ln_modulate(const float* __restrict__ x
     const int lane = threadIdx.x & 63;
     const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (row >= M) return;
-    const int nv = d / 4;
+    const int nv = EXACT ? 64 * MAXV : d / 4;
     const float* xr = x + (long)row * d;
     float4 v[MAXV];
 #pragma unroll
@@ -417,6 +420,11 @@ template <typename OT>
 static void launch_ln_modulate(int per_lane, dim3 grid, hipStream_t s, const float* x, int M, int d, RowGeom g,
                                int split, const float* mod, long mod_stride, int sh_a, int sc_a, int sh_b, int sc_b,
                                OT* out, float eps) {
+    if (d == 256 * 12) {   // the pages' width, 3072
+        hipLaunchKernelGGL((k_ln_modulate<OT, 12, true>), grid, dim3(256), 0, s, x, M, d, g, split, mod, mod_stride,
+                           sh_a, sc_a, sh_b, sc_b, out, eps);
+        return;
+    }
 #define AF_LNM(V) hipLaunchKernelGGL((k_ln_modulate<OT, V>), grid, dim3(256), 0, s, x, M, d, g, split, mod, \
                                      mod_stride, sh_a, sc_a, sh_b, sc_b, out, eps)
     if (per_lane <= 1) AF_LNM(1);
