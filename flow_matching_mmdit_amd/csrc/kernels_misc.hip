@@ -179,6 +179,81 @@ __global__ __launch_bounds__(256) void k_gemv_bf16(const float* __restrict__ x, 
     }
 }
 
+// bf16 weights with K a multiple of 512 (the modulation GEMV streams 4.6 GB of them
+// once per forward): the input vectors sit in LDS instead of registers, so a wave
+// holds only its R x NI weight chunks and six waves fit a SIMD; the weights are
+// read with non-temporal loads, as they are used once. Lane l's chunk i covers
+// k = 512 i + 8 l .. + 7, stored as two float4 at 512 i + 256 h + 4 l (h the
+// half), so each of a wave's 16-byte LDS reads is one contiguous 1 KB row.
+// Same summation order as k_gemv_bf16: results are bit-identical.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+template <int BC, int NI, int R>
+__global__ __launch_bounds__(256) void k_gemv_bf16_lds(const float* __restrict__ x, int B, int K,
+                                                       const bf16_t* __restrict__ W, int N,
+                                                       const bf16_t* __restrict__ bias, int silu_in,
+                                                       float* __restrict__ y, int b0) {
+    __shared__ float4 sx[BC][NI * 128];
+    const int lane = threadIdx.x & 63;
+    const int nb = min(BC, B - b0);
+    for (int idx = threadIdx.x; idx < BC * NI * 128; idx += blockDim.x) {
+        const int b = idx / (NI * 128), q = idx % (NI * 128);
+        const int k = 512 * (q / 128) + 8 * (q & 63) + 4 * ((q / 64) & 1);
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (b < nb) {
+            v = *reinterpret_cast<const float4*>(x + (long)(b0 + b) * K + k);
+            if (silu_in) v = make_float4(silu_f(v.x), silu_f(v.y), silu_f(v.z), silu_f(v.w));
+        }
+        sx[b][q] = v;
+    }
+    __syncthreads();
+    const int wave = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+    const int nwaves = (gridDim.x * blockDim.x) >> 6;
+    for (int n0 = wave * R; n0 < N; n0 += nwaves * R) {
+        asm volatile("" ::: "memory");   // keeps the LDS reads of x in the loop (not hoisted into registers)
+        uint4 w[R][NI];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const bf16_t* row = W + (long)min(n0 + r, N - 1) * K + 8 * lane;   // rows past N: read, unused
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                const u32x4_t t = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(row + 512 * i));
+                w[r][i] = make_uint4(t.x, t.y, t.z, t.w);
+            }
+        }
+        float acc[R][BC];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int b = 0; b < BC; ++b) acc[r][b] = 0.f;
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+#pragma unroll
+            for (int b = 0; b < BC; ++b) {
+                const float4 x0 = sx[b][128 * i + lane], x1 = sx[b][128 * i + 64 + lane];
+                const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const uint32_t u[4] = {w[r][i].x, w[r][i].y, w[r][i].z, w[r][i].w};
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        acc[r][b] += __uint_as_float(u[q] << 16) * xv[2 * q] +
+                                     __uint_as_float(u[q] & 0xFFFF0000u) * xv[2 * q + 1];
+                }
+            }
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+#pragma unroll
+            for (int b = 0; b < BC; ++b) acc[r][b] = wave_sum(acc[r][b]);
+            const int n = n0 + r;
+            if (lane == 0 && n < N) {
+                const float bb = bias ? bf2f(bias[n]) : 0.f;
+                for (int b = 0; b < nb; ++b) y[(long)(b0 + b) * N + n] = acc[r][b] + bb;
+            }
+        }
+    }
+}
+
 hipError_t gemv(const float* x, int B, int K, const void* W, af_dtype wdt, int N, const void* bias,
                 int silu_in, float* y, hipStream_t s) {
     if (B == 0 || N == 0) return hipSuccess;
@@ -192,12 +267,19 @@ hipError_t gemv(const float* x, int B, int K, const void* W, af_dtype wdt, int N
 #define AF_GEMV(NI, R)                                                                                       \
     hipLaunchKernelGGL((k_gemv_bf16<BC, NI, R>), dim3(min((N + 4 * R - 1) / (4 * R), 2048)), dim3(256), 0, s, x, \
                        B, K, Wb, N, bb, silu_in, y, b0)
-            if (ni <= 1) AF_GEMV(1, 4);
+#define AF_GEMV_LDS(NI, R)                                                                                        \
+    hipLaunchKernelGGL((k_gemv_bf16_lds<BC, NI, R>), dim3(min((N + 4 * R - 1) / (4 * R), 4096)), dim3(256), 0, s, \
+                       x, B, K, Wb, N, bb, silu_in, y, b0)
+            if (K % 512 == 0 && ni == 6) AF_GEMV_LDS(6, 4);
+            else if (K % 512 == 0 && ni == 8) AF_GEMV_LDS(8, 2);
+            else if (K % 512 == 0 && ni == 4) AF_GEMV_LDS(4, 4);
+            else if (ni <= 1) AF_GEMV(1, 4);
             else if (ni <= 2) AF_GEMV(2, 4);
             else if (ni <= 4) AF_GEMV(4, 4);
             else if (ni <= 6) AF_GEMV(6, 4);
             else AF_GEMV(8, 2);
 #undef AF_GEMV
+#undef AF_GEMV_LDS
         } else {
             int blocks = (N + 3) / 4;
             if (blocks > 4096) blocks = 4096;
