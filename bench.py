@@ -55,8 +55,9 @@ def forward_flops(d, F, L, B, S, T, Dtxt, Nimg, patch_dim):
     return B * L * per_block + B * (2 * T * Dtxt * d + 4 * Nimg * patch_dim * d)
 
 
-def class_work(name, d, F, B, S):
-    """(algorithmic FLOPs or bytes per launch, unit kind) for a kernel class."""
+def class_work(name, d, F, B, S, mod_rows=0):
+    """(algorithmic FLOPs or bytes per launch, unit kind) for a kernel class.
+    mod_rows: rows of the gathered modulation matrix (6 d per block and stream, 2 d final)."""
     M = B * S
     if name == "gemm_qkv":
         return 2.0 * M * d * 3 * d, "mfma"
@@ -70,6 +71,10 @@ def class_work(name, d, F, B, S):
         return 4.0 * B * S * S * d, "mfma"
     if name == "ln_modulate":
         return float(M * d * 4 + M * d * 2), "hbm"   # fp32 residual in, bf16 out
+    if name == "adaln" and mod_rows:
+        # bf16 weights of the timestep MLP (256 -> d -> d) and of every modulation row,
+        # each read once; the vectors in and out are a few MB
+        return float(2 * (d * 256 + d * d + mod_rows * d)), "hbm"
     return None, None
 
 
@@ -415,7 +420,8 @@ def main():
         for name, (kms, n) in prof.items():
             if n == 0:
                 continue
-            work, kind = class_work(name, d, F, B, S)
+            mod_rows = (2 * cfg.num_mmdit_layers + cfg.num_single_dit_layers) * 6 * d + 2 * d
+            work, kind = class_work(name, d, F, B, S, mod_rows)
             entry = {"ms_per_forward": kms / args.steps, "launches_per_forward": n / args.steps,
                      "avg_launch_ms": kms / n}
             if work is not None:
