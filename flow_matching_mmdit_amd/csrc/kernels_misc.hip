@@ -179,7 +179,7 @@ __global__ __launch_bounds__(256) void k_gemv_bf16(const float* __restrict__ x, 
     }
 }
 
-// bf16 weights with K a multiple of 512 (the modulation GEMV streams 4.6 GB of them
+// bf16 weights, K = 512 NI (the modulation GEMV streams 4.6 GB of them
 // once per forward): the input vectors sit in LDS instead of registers, so a wave
 // holds only its R x NI weight chunks and six waves fit a SIMD; the weights are
 // read with non-temporal loads, as they are used once. Lane l's chunk i covers
@@ -270,9 +270,7 @@ hipError_t gemv(const float* x, int B, int K, const void* W, af_dtype wdt, int N
 #define AF_GEMV_LDS(NI, R)                                                                                        \
     hipLaunchKernelGGL((k_gemv_bf16_lds<BC, NI, R>), dim3(min((N + 4 * R - 1) / (4 * R), 4096)), dim3(256), 0, s, \
                        x, B, K, Wb, N, bb, silu_in, y, b0)
-            if (K % 512 == 0 && ni == 6) AF_GEMV_LDS(6, 4);
-            else if (K % 512 == 0 && ni == 8) AF_GEMV_LDS(8, 2);
-            else if (K % 512 == 0 && ni == 4) AF_GEMV_LDS(4, 4);
+            if (K == 3072) AF_GEMV_LDS(6, 4);   // the pages' width (the instance the parity tests run)
             else if (ni <= 1) AF_GEMV(1, 4);
             else if (ni <= 2) AF_GEMV(2, 4);
             else if (ni <= 4) AF_GEMV(4, 4);
