@@ -539,7 +539,8 @@ hipError_t ln_modulate(const float* x, int M, int d, RowGeom g, int split, const
 // rounded to nearest even); scale bytes e + 127 in the [d/64][sc_rows][2] layout.
 // Lane l holds columns 4 (l + 64 i) .. + 3, so one 32-value block is the 8 lanes
 // 8q .. 8q + 7 of one i.
-template <int MAXV>
+// EXACT: d == 256 MAXV, the per-chunk conditions vanish (as in k_ln_modulate).
+template <int MAXV, bool EXACT = false>
 __global__ __launch_bounds__(256) void k_ln_modulate_mx(const float* __restrict__ x, int M, int d, RowGeom g,
                                                         int split, const float* __restrict__ mod, long mod_stride,
                                                         int sh_a, int sc_a, int sh_b, int sc_b,
@@ -548,7 +549,7 @@ __global__ __launch_bounds__(256) void k_ln_modulate_mx(const float* __restrict_
     const int lane = threadIdx.x & 63;
     const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (row >= M) return;
-    const int nv = d / 4;
+    const int nv = EXACT ? 64 * MAXV : d / 4;
     const float* xr = x + (long)row * d;
     float4 v[MAXV];
 #pragma unroll
@@ -575,16 +576,32 @@ __global__ __launch_bounds__(256) void k_ln_modulate_mx(const float* __restrict_
     const float* shp = mod + (long)bidx * mod_stride + (first ? sh_a : sh_b);
     const float* scp = mod + (long)bidx * mod_stride + (first ? sc_a : sc_b);
     uint8_t* orow = out + (long)row * d;
+    // every shift/scale load first, then y in place of v: the loads of all chunks
+    // are in flight together (the scale-byte stores below are a divergent branch
+    // per chunk, which loads inside the chunk loop could not be moved across)
+    float4 shv[MAXV], scv[MAXV];
 #pragma unroll
     for (int i = 0; i < MAXV; ++i) {
         const int c4 = lane + 64 * i;
         if (i * 64 < nv) {                   // uniform: d is a multiple of 256
-            const float4 sh = reinterpret_cast<const float4*>(shp)[c4];
-            const float4 s4 = reinterpret_cast<const float4*>(scp)[c4];
-            const float y0 = (v[i].x - mean) * rstd * (1.f + s4.x) + sh.x;
-            const float y1 = (v[i].y - mean) * rstd * (1.f + s4.y) + sh.y;
-            const float y2 = (v[i].z - mean) * rstd * (1.f + s4.z) + sh.z;
-            const float y3 = (v[i].w - mean) * rstd * (1.f + s4.w) + sh.w;
+            shv[i] = reinterpret_cast<const float4*>(shp)[c4];
+            scv[i] = reinterpret_cast<const float4*>(scp)[c4];
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i) {
+        if (i * 64 < nv) {
+            v[i].x = (v[i].x - mean) * rstd * (1.f + scv[i].x) + shv[i].x;
+            v[i].y = (v[i].y - mean) * rstd * (1.f + scv[i].y) + shv[i].y;
+            v[i].z = (v[i].z - mean) * rstd * (1.f + scv[i].z) + shv[i].z;
+            v[i].w = (v[i].w - mean) * rstd * (1.f + scv[i].w) + shv[i].w;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i) {
+        const int c4 = lane + 64 * i;
+        if (i * 64 < nv) {
+            const float y0 = v[i].x, y1 = v[i].y, y2 = v[i].z, y3 = v[i].w;
             float amax = fmaxf(fmaxf(fabsf(y0), fabsf(y1)), fmaxf(fabsf(y2), fabsf(y3)));
             amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
             amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
@@ -609,6 +626,11 @@ hipError_t ln_modulate_mx(const float* x, int M, int d, RowGeom g, int split, co
 #define AF_LNMX(V) hipLaunchKernelGGL((k_ln_modulate_mx<V>), grid, dim3(256), 0, s, x, M, d, g, split, mod, mod_stride, \
                                       sh_a, sc_a, sh_b, sc_b, out, sc, sc_rows, eps)
     const int per_lane = d / 256;
+    if (d == 256 * 12) {   // the pages' width, 3072
+        hipLaunchKernelGGL((k_ln_modulate_mx<12, true>), grid, dim3(256), 0, s, x, M, d, g, split, mod, mod_stride,
+                           sh_a, sc_a, sh_b, sc_b, out, sc, sc_rows, eps);
+        return hipGetLastError();
+    }
     if (per_lane <= 4) AF_LNMX(4);
     else if (per_lane <= 8) AF_LNMX(8);
     else if (per_lane <= 12) AF_LNMX(12);
