@@ -140,3 +140,81 @@ def test_mx_forward_uses_quantized_operands_only_where_stated():
         assert not np.array_equal(qb[k], blk[k])
         np.testing.assert_array_equal(qb[k], oracle.mxfp8_qdq(blk[k]))
     np.testing.assert_array_equal(oracle.mxfp8_qdq(qb["ff3"]), qb["ff3"])
+
+
+def _single_block_by_hand(cfg, blk, temb, x, kv, quant_points):
+    """A single DiT block with MXFP8 quantize-dequantize applied exactly at the
+    named activation points (a subset of 'ln1', 'attn', 'ln2', 'ffh') and to the
+    weights of the QKV, out-projection and FFN products; everything else in
+    float32. Composed from the block's equations: adaLN-Zero with six vectors,
+    LN + modulate, bias-free q/k/v with per-head LayerNorm, softmax attention,
+    gated out-projection, LN + modulate, SiLU-gated FFN, gated residual."""
+    f32 = np.float32
+    qd = lambda a, point: oracle.mxfp8_qdq(a) if point in quant_points else a
+    Wq = {k: oracle.mxfp8_qdq(blk[k]) for k in ("wq", "wk", "wv", "wo", "ff1", "ff2", "ff3")}
+    d = cfg.inner_dim
+    H, hd = cfg.num_attention_heads, cfg.attention_head_dim
+    eps = f32(cfg.ln_eps)
+    mod = T.silu(temb) @ blk["ada"].T
+    sh1, sc1, g1, sh2, sc2, g2 = (mod[:, i * d:(i + 1) * d] for i in range(6))
+    B, S, _ = x.shape
+    n1 = qd(T.layer_norm(x, eps) * (1 + sc1[:, None, :]) + sh1[:, None, :], "ln1")
+    heads = lambda y: y.reshape(B, S, H, hd).transpose(0, 2, 1, 3)
+    q = T.layer_norm(heads(n1 @ Wq["wq"].T), eps)
+    k = T.layer_norm(heads(n1 @ Wq["wk"].T), eps)
+    v = heads(n1 @ Wq["wv"].T)
+    o = T.attention(q, k, v, kv, f32(1.0 / np.sqrt(hd)))
+    o = qd(o.transpose(0, 2, 1, 3).reshape(B, S, d), "attn")
+    x1 = x + g1[:, None, :] * (o @ Wq["wo"].T)
+    n2 = qd(T.layer_norm(x1, eps) * (1 + sc2[:, None, :]) + sh2[:, None, :], "ln2")
+    h = qd(T.silu(n2 @ Wq["ff1"].T) * (n2 @ Wq["ff2"].T), "ffh")
+    return x1 + g2[:, None, :] * (h @ Wq["ff3"].T)
+
+
+def test_mx_single_block_quantizes_exactly_the_four_activation_points():
+    """single_block(mx=True) equals the block composed by hand with MXFP8 applied at
+    the LN + modulate outputs (both), the attention output and the FFN hidden
+    activations, and at no other activation; dropping any one of the four points
+    changes the result, so each of them is pinned."""
+    cfg = oracle.TINY
+    W = oracle.Weights.seeded(cfg, seed=0)
+    rng = np.random.default_rng(11)
+    B, T_, N = 2, 8, 64
+    d = cfg.inner_dim
+    temb = rng.standard_normal((B, d)).astype(np.float32)
+    x = rng.standard_normal((B, cfg.num_register_tokens + T_ + N, d)).astype(np.float32)
+    kv = np.ones((B, x.shape[1]), np.uint8)
+    kv[1, cfg.num_register_tokens + 5:cfg.num_register_tokens + T_] = 0
+    blk = {k: W["single0." + k] for k in ("ada", "wq", "wk", "wv", "wo", "ff1", "ff2", "ff3")}
+    # adaLN rows scaled up so the gates and modulations are O(1) and every branch
+    # moves the residual visibly
+    blk["ada"] = blk["ada"] * np.float32(20.0)
+    points = ("ln1", "attn", "ln2", "ffh")
+    got = T.single_block(cfg, blk, temb, x, kv, np.float32, mx=True)
+    want = _single_block_by_hand(cfg, blk, temb, x, kv, points)
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-5 * np.abs(want).max())
+    for drop in points:
+        other = _single_block_by_hand(cfg, blk, temb, x, kv, tuple(p for p in points if p != drop))
+        # quantization moves the block output by far more than the tolerance above
+        assert np.abs(other - want).max() > 1e-3 * np.abs(want - x).max(), drop
+
+
+def test_mx_joint_block_quantizes_the_same_points_per_stream():
+    """A joint block whose two streams carry identical weights equals the single
+    block over the concatenated sequence in mx mode as well (so the joint block
+    quantizes the same four points in each stream)."""
+    cfg = oracle.TINY
+    W = oracle.Weights.seeded(cfg, seed=0)
+    rng = np.random.default_rng(12)
+    B, T_, N = 1, 8, 64
+    d = cfg.inner_dim
+    Nt = cfg.num_register_tokens + T_
+    temb = rng.standard_normal((B, d)).astype(np.float32)
+    x = rng.standard_normal((B, Nt + N, d)).astype(np.float32)
+    kv = np.ones((B, x.shape[1]), np.uint8)
+    blk = {k: W["single0." + k] for k in ("ada", "wq", "wk", "wv", "wo", "ff1", "ff2", "ff3")}
+    blk["ada"] = blk["ada"] * np.float32(20.0)
+    xt, xi = T.joint_block(cfg, blk, blk, temb, x[:, :Nt], x[:, Nt:], kv, np.float32, mx=True)
+    want = _single_block_by_hand(cfg, blk, temb, x, kv, ("ln1", "attn", "ln2", "ffh"))
+    got = np.concatenate([xt, xi], 1)
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-5 * np.abs(want).max())

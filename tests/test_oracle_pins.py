@@ -421,6 +421,31 @@ def test_identity_model_returns_latents():
     np.testing.assert_array_equal(out, lat)
 
 
+def test_identity_model_routes_the_patch_bias_to_its_pixels():
+    """Patch embedding has a bias ([TRANS] 核心子模块架构, Patch Embedding: the
+    projection is an nn.Linear written without bias=False). In the identity model
+    a bias b on the patch features reaches the output through the (c, py, px) ->
+    (py, px, c) permutation of proj_out, so pixel (c, y, x) gains
+    b[c p^2 + (y mod p) p + (x mod p)]; written out element by element."""
+    cfg = replace(oracle.TINY, num_attention_heads=2, attention_head_dim=8, caption_projection_dim=16)
+    rng = np.random.default_rng(15)
+    tensors = _identity_model_weights(cfg, rng)
+    d, p = cfg.inner_dim, cfg.patch_size
+    bias = (np.arange(d) * 0.25 - 1.5).astype(np.float32)     # distinct, exactly representable
+    tensors["pe_b"] = bias
+    W = oracle.Weights.from_dict(cfg, tensors)
+    H_, W_ = 6, 10
+    lat = rng.standard_normal((2, 4, H_, W_)).astype(np.float32)
+    text = rng.standard_normal((2, 3, cfg.joint_attention_dim)).astype(np.float32)
+    out = oracle.forward(cfg, W, lat, np.array([0.2, 0.7]), text, None, F64)
+    for b in range(2):
+        for c in range(4):
+            for y in range(H_):
+                for x in range(W_):
+                    want = float(lat[b, c, y, x]) + float(bias[c * p * p + (y % p) * p + (x % p)])
+                    assert out[b, c, y, x] == want, (b, c, y, x)
+
+
 def test_identity_model_places_the_cropped_position_table():
     cfg = replace(oracle.TINY, num_attention_heads=2, attention_head_dim=8, caption_projection_dim=16)
     rng = np.random.default_rng(14)
