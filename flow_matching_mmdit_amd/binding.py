@@ -65,6 +65,7 @@ def _load():
         "af_transformer_forward": (I, [P, P, P, P, I, P, I, I, I, I, P, P]),
         "af_transformer_forward_taps": (I, [P, P, P, P, I, P, I, I, I, I, I, P, P]),
         "af_flow_euler_cfg_step": (I, [P, P, I, I, I, I, F, F, F, P]),
+        "af_flow_cfg_inputs": (I, [P, I, I, I, I, F, I, P, P, P]),
         "af_sigma_schedule": (I, [I, D, C.POINTER(F)]),
         "af_destroy": (V, [P]),
         "af_status_string": (C.c_char_p, [I]),
@@ -90,7 +91,7 @@ _lib = _load()
 EXPORTED = (
     "af_config_default", "af_check_shapes", "af_weight_count", "af_weight_info", "af_create",
     "af_load_weights", "af_init_weights", "af_transformer_forward", "af_transformer_forward_taps",
-    "af_flow_euler_cfg_step", "af_sigma_schedule", "af_destroy", "af_status_string",
+    "af_flow_euler_cfg_step", "af_flow_cfg_inputs", "af_sigma_schedule", "af_destroy", "af_status_string",
     "af_last_error", "af_umt5_config_default", "af_umt5_weight_count", "af_umt5_weight_info",
     "af_umt5_create", "af_umt5_load_weights", "af_umt5_encode", "af_umt5_encode_taps", "af_umt5_destroy")
 
@@ -142,13 +143,52 @@ def af_sigma_schedule(num_steps: int, shift: float) -> np.ndarray:
     return np.frombuffer(out, dtype=np.float32).copy()
 
 
+def _need(cond, msg):
+    """Argument check on the host, before anything is enqueued (a failed check
+    raises ValueError, as the library's own shape errors do)."""
+    if not cond:
+        raise ValueError(msg)
+
+
+def _on_device(t, name, device):
+    _need(t.is_cuda and (device is None or t.device.index == device),
+          f"{name} must be a tensor on cuda:{'' if device is None else device}")
+
+
 def af_flow_euler_cfg_step(latents, v, sigma: float, sigma_next: float, guidance: float, stream=None):
+    """x <- x + (sigma_next - sigma) * v_hat in place; v holds [uncond; cond] (2 Bi
+    samples) when guidance > 1, else Bi samples."""
     import torch
-    assert latents.dtype == torch.float32 and v.dtype == torch.float32
-    assert latents.is_contiguous() and v.is_contiguous() and latents.dim() == 4
+    _need(latents.dtype == torch.float32 and v.dtype == torch.float32, "latents and v must be float32")
+    _need(latents.is_contiguous() and v.is_contiguous(), "latents and v must be contiguous")
+    _need(latents.dim() == 4, "latents must be [Bi, C, H, W]")
+    per = 2 if guidance > 1.0 else 1
+    _need(v.numel() == per * latents.numel(),
+          f"v must hold {per} x latents.numel() values (guidance {guidance})")
+    _on_device(latents, "latents", None)
+    _on_device(v, "v", latents.device.index)
     Bi, Cc, H, W = latents.shape
     _check(_lib.af_flow_euler_cfg_step(C.c_void_p(latents.data_ptr()), C.c_void_p(v.data_ptr()), Bi, Cc, H, W,
                                        sigma, sigma_next, guidance, _stream_ptr(stream)))
+
+
+def af_flow_cfg_inputs(latents, sigma: float, cfg_on: bool, x_in, tau, stream=None):
+    """x_in = [latents; latents] (cfg_on) or latents, tau[:] = sigma (one CFG step's
+    transformer inputs)."""
+    import torch
+    _need(latents.dtype == torch.float32 and x_in.dtype == torch.float32 and tau.dtype == torch.float32,
+          "latents, x_in and tau must be float32")
+    _need(latents.is_contiguous() and x_in.is_contiguous() and tau.is_contiguous(), "tensors must be contiguous")
+    _need(latents.dim() == 4, "latents must be [Bi, C, H, W]")
+    per = 2 if cfg_on else 1
+    Bi, Cc, H, W = latents.shape
+    _need(tuple(x_in.shape) == (per * Bi, Cc, H, W), "x_in must be [(2 if cfg_on else 1) * Bi, C, H, W]")
+    _need(tau.numel() == per * Bi, "tau must hold one value per x_in sample")
+    _on_device(latents, "latents", None)
+    for t, name in ((x_in, "x_in"), (tau, "tau")):
+        _on_device(t, name, latents.device.index)
+    _check(_lib.af_flow_cfg_inputs(C.c_void_p(latents.data_ptr()), Bi, Cc, H, W, sigma, 1 if cfg_on else 0,
+                                   C.c_void_p(x_in.data_ptr()), C.c_void_p(tau.data_ptr()), _stream_ptr(stream)))
 
 
 def _stream_ptr(stream=None):
@@ -227,26 +267,18 @@ class AuraFlowModel:
                 for off, a in ex.map(draw, range(w0, min(n, w0 + win))):
                     self.load_weights(a, off)
 
-    def _common(self, latents, tau, text, mask):
-        import torch
-        B, Cc, H, W = latents.shape
-        T = text.shape[1]
-        assert latents.dtype == torch.float32 and latents.is_contiguous() and latents.is_cuda
-        assert tau.dtype == torch.float32 and tau.is_contiguous() and tau.numel() == B
-        assert text.is_contiguous() and text.shape[0] == B and text.shape[2] == self.cfg.joint_attention_dim
-        tdt = AF_BF16 if text.dtype == torch.bfloat16 else AF_F32
-        assert text.dtype in (torch.bfloat16, torch.float32)
-        mptr = None
-        if mask is not None:
-            assert mask.dtype == torch.uint8 and mask.is_contiguous() and tuple(mask.shape) == (B, T)
-            mptr = C.c_void_p(mask.data_ptr())
-        return B, Cc, H, W, T, tdt, mptr
+    def _common(self, latents, tau, text, mask, out=None, out_shape=None):
+        """Host-side checks of the tensor arguments (dtype, layout, shape, device)
+        before anything is enqueued; returns the ABI's size arguments."""
+        return check_forward_tensors(self.cfg, self.device, latents, tau, text, mask, out, out_shape)
 
     def forward(self, latents, tau, text, mask=None, out=None, stream=None):
         import torch
-        B, Cc, H, W, T, tdt, mptr = self._common(latents, tau, text, mask)
+        B, Cc, H, W = latents.shape if latents.dim() == 4 else (0, 0, 0, 0)
+        oshape = (B, self.cfg.out_channels, H, W)
+        B, Cc, H, W, T, tdt, mptr = self._common(latents, tau, text, mask, out, oshape)
         if out is None:
-            out = torch.empty((B, self.cfg.out_channels, H, W), dtype=torch.float32, device=latents.device)
+            out = torch.empty(oshape, dtype=torch.float32, device=latents.device)
         _check(_lib.af_transformer_forward(self._h, C.c_void_p(latents.data_ptr()), C.c_void_p(tau.data_ptr()),
                                            C.c_void_p(text.data_ptr()), tdt, mptr, B, H, W, T,
                                            C.c_void_p(out.data_ptr()), _stream_ptr(stream)))
@@ -254,10 +286,13 @@ class AuraFlowModel:
 
     def forward_taps(self, latents, tau, text, mask=None, stop_after_block: int = 0, out=None, stream=None):
         import torch
-        B, Cc, H, W, T, tdt, mptr = self._common(latents, tau, text, mask)
-        S = self.cfg.num_register_tokens + T + (H // self.cfg.patch_size) * (W // self.cfg.patch_size)
+        _need(latents.dim() == 4 and text.dim() == 3, "latents must be [B, C, H, W] and text [B, T, D]")
+        B, Cc, H, W = latents.shape
+        S = self.cfg.num_register_tokens + text.shape[1] + (H // self.cfg.patch_size) * (W // self.cfg.patch_size)
+        oshape = (B, S, self.inner_dim)
+        B, Cc, H, W, T, tdt, mptr = self._common(latents, tau, text, mask, out, oshape)
         if out is None:
-            out = torch.empty((B, S, self.inner_dim), dtype=torch.float32, device=latents.device)
+            out = torch.empty(oshape, dtype=torch.float32, device=latents.device)
         _check(_lib.af_transformer_forward_taps(self._h, C.c_void_p(latents.data_ptr()), C.c_void_p(tau.data_ptr()),
                                                 C.c_void_p(text.data_ptr()), tdt, mptr, B, H, W, T,
                                                 stop_after_block, C.c_void_p(out.data_ptr()), _stream_ptr(stream)))
@@ -266,23 +301,63 @@ class AuraFlowModel:
     def sample(self, x, text, mask=None, num_steps: int = 25, shift: float = 1.73, guidance: float = 3.5,
                stream=None):
         """Flow-matching Euler sampling loop with CFG. x: [B', C, H, W] (updated in place);
-        text/mask: [2B', ...] = [uncond; cond] when guidance > 1, else [B', ...]."""
+        text/mask: [2B', ...] = [uncond; cond] when guidance > 1, else [B', ...].
+        Every step runs as three library calls on one stream: the step's inputs
+        (latents duplicated for CFG, tau = sigma_i), the forward and the CFG + Euler
+        update. With `stream` given, the buffers are also allocated on it."""
+        import contextlib
         import torch
         sig = af_sigma_schedule(num_steps, shift)
         Bp = x.shape[0]
         cfg_on = guidance > 1.0
         Bt = 2 * Bp if cfg_on else Bp
-        xin = torch.empty((Bt,) + tuple(x.shape[1:]), dtype=torch.float32, device=x.device)
-        tau = torch.empty(Bt, dtype=torch.float32, device=x.device)
-        v = torch.empty_like(xin)
-        for i in range(num_steps):
-            xin[:Bp].copy_(x)
-            if cfg_on:
-                xin[Bp:].copy_(x)
-            tau.fill_(float(sig[i]))
-            self.forward(xin, tau, text, mask, out=v, stream=stream)
-            af_flow_euler_cfg_step(x, v, float(sig[i]), float(sig[i + 1]), guidance, stream)
+        _need(text.shape[0] == Bt, f"text must hold {Bt} rows ([uncond; cond] when guidance > 1)")
+        ctx = torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+        with ctx:
+            s = torch.cuda.current_stream()
+            xin = torch.empty((Bt,) + tuple(x.shape[1:]), dtype=torch.float32, device=x.device)
+            tau = torch.empty(Bt, dtype=torch.float32, device=x.device)
+            v = torch.empty_like(xin)
+            for i in range(num_steps):
+                af_flow_cfg_inputs(x, float(sig[i]), cfg_on, xin, tau, stream=s)
+                self.forward(xin, tau, text, mask, out=v, stream=s)
+                af_flow_euler_cfg_step(x, v, float(sig[i]), float(sig[i + 1]), guidance, stream=s)
         return x
+
+
+def check_forward_tensors(cfg: AfConfig, device: int, latents, tau, text, mask=None, out=None, out_shape=None):
+    """Checks the tensor arguments of a forward against the model's config: dtype,
+    contiguity and shape of every tensor first, then that every tensor (out
+    included) lives on cuda:`device`. Raises ValueError before anything is
+    enqueued; returns (B, C, H, W, T, text dtype code, mask pointer or None)."""
+    import torch
+    _need(latents.dim() == 4, "latents must be [B, C, H, W]")
+    B, Cc, H, W = latents.shape
+    _need(latents.dtype == torch.float32 and latents.is_contiguous(), "latents must be contiguous float32")
+    _need(Cc == cfg.in_channels, f"latents must have {cfg.in_channels} channels")
+    _need(tau.dtype == torch.float32 and tau.is_contiguous() and tau.numel() == B,
+          "tau must be contiguous float32 with one value per sample")
+    _need(text.dim() == 3 and text.shape[0] == B and text.shape[2] == cfg.joint_attention_dim,
+          f"text must be [B, T, {cfg.joint_attention_dim}]")
+    _need(text.dtype in (torch.bfloat16, torch.float32) and text.is_contiguous(),
+          "text must be contiguous bfloat16 or float32")
+    T = text.shape[1]
+    if mask is not None:
+        _need(mask.dtype == torch.uint8 and mask.is_contiguous() and tuple(mask.shape) == (B, T),
+              "mask must be contiguous uint8 [B, T]")
+    if out is not None:
+        _need(out.dtype == torch.float32 and out.is_contiguous(), "out must be contiguous float32")
+        _need(out_shape is None or tuple(out.shape) == tuple(out_shape), f"out must have shape {tuple(out_shape)}")
+    named = [(latents, "latents"), (tau, "tau"), (text, "text")]
+    if mask is not None:
+        named.append((mask, "mask"))
+    if out is not None:
+        named.append((out, "out"))
+    for t, name in named:
+        _on_device(t, name, device)
+    tdt = AF_BF16 if text.dtype == torch.bfloat16 else AF_F32
+    mptr = C.c_void_p(mask.data_ptr()) if mask is not None else None
+    return B, Cc, H, W, T, tdt, mptr
 
 
 # ----------------------------------------------------------------------------- diagnostics
@@ -399,19 +474,30 @@ class UMT5Encoder:
 
     def _args(self, ids, mask):
         import torch
-        assert ids.dtype == torch.int32 and ids.is_contiguous() and ids.is_cuda and ids.dim() == 2
+        _need(ids.dtype == torch.int32 and ids.is_contiguous() and ids.dim() == 2, "ids must be contiguous int32 [B, T]")
         B, T = ids.shape
         mptr = None
         if mask is not None:
-            assert mask.dtype == torch.uint8 and mask.is_contiguous() and tuple(mask.shape) == (B, T)
+            _need(mask.dtype == torch.uint8 and mask.is_contiguous() and tuple(mask.shape) == (B, T),
+                  "mask must be contiguous uint8 [B, T]")
             mptr = C.c_void_p(mask.data_ptr())
+        _on_device(ids, "ids", self.device)
+        if mask is not None:
+            _on_device(mask, "mask", self.device)
         return B, T, mptr
+
+    def _check_out(self, out, B, T):
+        import torch
+        _need(out.dtype == torch.float32 and out.is_contiguous() and tuple(out.shape) == (B, T, self.cfg.d_model),
+              "out must be contiguous float32 [B, T, d_model]")
+        _on_device(out, "out", self.device)
 
     def encode(self, ids, mask=None, out=None, stream=None):
         import torch
         B, T, mptr = self._args(ids, mask)
         if out is None:
             out = torch.empty((B, T, self.cfg.d_model), dtype=torch.float32, device=ids.device)
+        self._check_out(out, B, T)
         _check(_lib.af_umt5_encode(self._h, C.c_void_p(ids.data_ptr()), mptr, B, T, C.c_void_p(out.data_ptr()),
                                    _stream_ptr(stream)))
         return out
@@ -421,6 +507,7 @@ class UMT5Encoder:
         B, T, mptr = self._args(ids, mask)
         if out is None:
             out = torch.empty((B, T, self.cfg.d_model), dtype=torch.float32, device=ids.device)
+        self._check_out(out, B, T)
         _check(_lib.af_umt5_encode_taps(self._h, C.c_void_p(ids.data_ptr()), mptr, B, T, stop_after_layer,
                                         C.c_void_p(out.data_ptr()), _stream_ptr(stream)))
         return out

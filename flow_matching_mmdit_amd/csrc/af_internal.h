@@ -105,6 +105,9 @@ hipError_t prefinal_project(const float* resid, RowGeom g, int d, const float* m
                             int h, int w, float* out, hipStream_t s);
 hipError_t euler_cfg(float* x, const float* v, long n, float dt, float guidance, int cfg_on,
                      hipStream_t s);
+// xin = [x; x] (cfg_on) or x, n elements per copy; tau[0 .. (cfg_on ? 2 Bi : Bi)) = sigma
+hipError_t cfg_inputs(const float* x, long n, int Bi, int cfg_on, float sigma, float* xin, float* tau,
+                      hipStream_t s);
 enum PackLayout { PACK_PLAIN = 0, PACK_FFN_GATE = 1, PACK_FFN_UP = 2 };
 // Converts src[0, n) (a slice of one canonical tensor starting at element `first`) into dst.
 hipError_t pack_weights(const float* src, long n, long first, void* dst, af_dtype ddt, int layout,

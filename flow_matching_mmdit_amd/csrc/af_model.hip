@@ -986,6 +986,20 @@ af_status af_flow_euler_cfg_step(float* latents, const float* v, int Bi, int C, 
     return AF_OK;
 }
 
+af_status af_flow_cfg_inputs(const float* latents, int Bi, int C, int H, int W, float sigma, int cfg_on,
+                             float* x_in, float* tau, void* stream) {
+    if (Bi < 0 || C < 0 || H < 0 || W < 0) return fail(AF_E_INVALID_ARG, "negative size");
+    const long n = (long)Bi * C * H * W;
+    if (Bi == 0) return AF_OK;
+    if (!latents || !x_in || !tau) return fail(AF_E_INVALID_ARG, "NULL device pointer");
+    if (!std::isfinite(sigma)) return fail(AF_E_INVALID_ARG, "non-finite sigma");
+    const long nin = cfg_on ? 2 * n : n;
+    if ((const float*)x_in < latents + n && latents < (const float*)x_in + nin)
+        return fail(AF_E_INVALID_ARG, "x_in overlaps latents");
+    AF_K(cfg_inputs(latents, n, Bi, cfg_on ? 1 : 0, sigma, x_in, tau, (hipStream_t)stream));
+    return AF_OK;
+}
+
 af_status af_sigma_schedule(int num_steps, double shift, float* out) {
     if (num_steps <= 0) return fail(AF_E_INVALID_ARG, "num_steps must be positive");
     if (!out) return fail(AF_E_INVALID_ARG, "output is NULL");

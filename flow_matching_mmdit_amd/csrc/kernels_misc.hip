@@ -821,6 +821,36 @@ hipError_t euler_cfg(float* x, const float* v, long n, float dt, float guidance,
     return hipGetLastError();
 }
 
+// x_in = [x; x] (cfg_on) or [x], tau[:] = sigma. vec: n % 4 == 0 and both
+// pointers 16-byte aligned, one float4 per thread; otherwise one element per
+// thread. The grid covers max(copy work, nt) threads.
+__global__ void k_cfg_inputs(const float* __restrict__ x, long n, int cfg_on, float sigma, float* __restrict__ xin,
+                             float* __restrict__ tau, int nt, int vec) {
+    const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < nt) tau[i] = sigma;
+    if (vec) {
+        if (4 * i < n) {
+            const float4 v = reinterpret_cast<const float4*>(x)[i];
+            reinterpret_cast<float4*>(xin)[i] = v;
+            if (cfg_on) reinterpret_cast<float4*>(xin + n)[i] = v;
+        }
+    } else if (i < n) {
+        xin[i] = x[i];
+        if (cfg_on) xin[n + i] = x[i];
+    }
+}
+
+hipError_t cfg_inputs(const float* x, long n, int Bi, int cfg_on, float sigma, float* xin, float* tau,
+                      hipStream_t s) {
+    if (n == 0) return hipSuccess;
+    const int nt = cfg_on ? 2 * Bi : Bi;
+    const int vec = (n % 4 == 0) && (((uintptr_t)x | (uintptr_t)xin) % 16 == 0);
+    const long work = std::max<long>(vec ? n / 4 : n, nt);
+    hipLaunchKernelGGL(k_cfg_inputs, dim3((unsigned)((work + 255) / 256)), dim3(256), 0, s, x, n, cfg_on, sigma, xin,
+                       tau, nt, vec);
+    return hipGetLastError();
+}
+
 // ============================================================================ weight packing
 // Canonical fp32 tensors -> device layout. FFN gate/up rows are interleaved in
 // 32-row groups ([F, d] gate rows f -> packed row (f/32)*64 + f%32, up rows ->

@@ -193,6 +193,20 @@ af_status af_flow_euler_cfg_step(float* latents, const float* v, int Bi, int C, 
                                  float sigma, float sigma_next, float guidance, void* stream);
 
 /*
+ * Inputs of one CFG denoising step of the sampling loop ([TRANS] 在
+ * AuraFlowPipeline 中的实际调用: the latents are duplicated for the (uncond,
+ * cond) halves and every sample gets the step's timestep t/1000 = sigma):
+ *   latents  device fp32 [Bi, C, H, W] (read only)
+ *   x_in     device fp32; cfg_on != 0: [2 Bi, C, H, W] = [latents; latents],
+ *            otherwise [Bi, C, H, W] = latents
+ *   tau      device fp32 [2 Bi] (cfg_on != 0) or [Bi], every entry = sigma
+ * x_in must not overlap latents. Bi == 0 is a no-op. Errors: negative sizes,
+ * NULL pointers with Bi > 0, non-finite sigma -> AF_E_INVALID_ARG.
+ */
+af_status af_flow_cfg_inputs(const float* latents, int Bi, int C, int H, int W, float sigma, int cfg_on,
+                             float* x_in, float* tau, void* stream);
+
+/*
  * Flow-matching sigma schedule (host): sigmas_out[i] for i = 0..num_steps,
  * u_i = 1 - i / num_steps mapped through shift * u / (1 + (shift - 1) u)
  * ([DEEP] section 2.3: shift 1.73, 1000 train timesteps). sigmas_out has

@@ -192,3 +192,84 @@ def test_umt5_default_config_matches_pages(af):
     # [DEEP] 2.1 文本编码器: d_model 2048, 32 heads, 24 layers, d_ff 5120, vocab 32128, max distance 128
     assert (c.d_model, c.num_heads, c.num_layers, c.d_ff, c.vocab_size, c.rel_max_distance) == \
         (2048, 32, 24, 5120, 32128, 128)
+
+
+# ----------------------------------------------------------------------------- binding argument checks
+# Each bad argument raises ValueError in the binding, before the library is
+# called (CPU tensors stand in; no model handle and no device are needed).
+
+def _good(af, B=2, T=16, H=32, W=32):
+    import torch
+    cfg = _cfg(af)
+    lat = torch.zeros((B, 4, H, W), dtype=torch.float32)
+    tau = torch.zeros(B, dtype=torch.float32)
+    text = torch.zeros((B, T, cfg.joint_attention_dim), dtype=torch.bfloat16)
+    mask = torch.ones((B, T), dtype=torch.uint8)
+    out = torch.zeros((B, 4, H, W), dtype=torch.float32)
+    return cfg, lat, tau, text, mask, out
+
+
+@pytest.mark.parametrize("bad", ["tau_len", "tau_dtype", "text_dim", "text_batch", "text_dtype", "mask_shape",
+                                 "mask_dtype", "out_shape", "out_dtype", "lat_channels", "lat_rank", "noncontig"])
+def test_forward_tensor_checks_raise_before_launch(af, bad):
+    import torch
+    cfg, lat, tau, text, mask, out = _good(af)
+    if bad == "tau_len": tau = torch.zeros(3)
+    if bad == "tau_dtype": tau = tau.double()
+    if bad == "text_dim": text = torch.zeros((2, 16, 1024), dtype=torch.bfloat16)
+    if bad == "text_batch": text = torch.zeros((1, 16, 2048), dtype=torch.bfloat16)
+    if bad == "text_dtype": text = text.half()
+    if bad == "mask_shape": mask = torch.ones((2, 15), dtype=torch.uint8)
+    if bad == "mask_dtype": mask = mask.bool()
+    if bad == "out_shape": out = torch.zeros((2, 4, 32, 16))
+    if bad == "out_dtype": out = out.half()
+    if bad == "lat_channels": lat = torch.zeros((2, 3, 32, 32))
+    if bad == "lat_rank": lat = torch.zeros((2, 4, 32))
+    if bad == "noncontig": lat = torch.zeros((2, 4, 32, 64))[..., ::2]
+    with pytest.raises(ValueError) as e:
+        af.check_forward_tensors(cfg, 0, lat, tau, text, mask, out, (2, 4, 32, 32))
+    assert "cuda" not in str(e.value), e.value   # a shape/dtype error, reported before the device check
+
+
+@pytest.mark.parametrize("where", ["latents", "tau", "text", "mask", "out"])
+def test_forward_tensor_checks_reject_host_tensors(af, where):
+    """Well-formed arguments that are not on the model's device are refused (a host
+    pointer handed to a kernel would fault the GPU)."""
+    cfg, lat, tau, text, mask, out = _good(af)
+    with pytest.raises(ValueError, match="must be a tensor on cuda:0") as e:
+        af.check_forward_tensors(cfg, 0, lat, tau, text, mask, out, (2, 4, 32, 32))
+    assert "latents" in str(e.value)             # the first tensor checked is named
+
+
+def test_euler_and_cfg_input_wrappers_check_sizes_before_launch(af):
+    import torch
+    x = torch.zeros((2, 4, 8, 8))
+    with pytest.raises(ValueError, match="v must hold 2"):
+        af.af_flow_euler_cfg_step(x, torch.zeros((2, 4, 8, 8)), 1.0, 0.5, 3.5)      # CFG needs [uncond; cond]
+    with pytest.raises(ValueError, match="v must hold 1"):
+        af.af_flow_euler_cfg_step(x, torch.zeros((4, 4, 8, 8)), 1.0, 0.5, 1.0)
+    with pytest.raises(ValueError, match="must be a tensor on cuda"):
+        af.af_flow_euler_cfg_step(x, torch.zeros((4, 4, 8, 8)), 1.0, 0.5, 3.5)      # sizes fine, host memory
+    with pytest.raises(ValueError, match="x_in must be"):
+        af.af_flow_cfg_inputs(x, 0.5, True, torch.zeros((2, 4, 8, 8)), torch.zeros(4))
+    with pytest.raises(ValueError, match="tau must hold"):
+        af.af_flow_cfg_inputs(x, 0.5, True, torch.zeros((4, 4, 8, 8)), torch.zeros(2))
+    with pytest.raises(ValueError, match="must be a tensor on cuda"):
+        af.af_flow_cfg_inputs(x, 0.5, False, torch.zeros((2, 4, 8, 8)), torch.zeros(2))
+
+
+def test_cfg_inputs_library_argument_errors_without_device(af):
+    """The library's own checks (NULL pointers, negative sizes, non-finite sigma,
+    overlapping buffers) reject before anything is enqueued."""
+    import ctypes as C
+    lib = af._lib
+    assert lib.af_flow_cfg_inputs(None, 0, 4, 8, 8, 0.5, 1, None, None, None) == af.AF_OK       # Bi = 0: no-op
+    assert lib.af_flow_cfg_inputs(None, 1, 4, 8, 8, 0.5, 1, None, None, None) == af.AF_E_INVALID_ARG
+    assert lib.af_flow_cfg_inputs(C.c_void_p(256), -1, 4, 8, 8, 0.5, 1, C.c_void_p(4096), C.c_void_p(8192),
+                                  None) == af.AF_E_INVALID_ARG
+    assert lib.af_flow_cfg_inputs(C.c_void_p(256), 1, 4, 8, 8, float("nan"), 1, C.c_void_p(1 << 20),
+                                  C.c_void_p(1 << 21), None) == af.AF_E_INVALID_ARG
+    # x_in starting inside latents (256 floats each) overlaps
+    assert lib.af_flow_cfg_inputs(C.c_void_p(4096), 1, 4, 8, 8, 0.5, 0, C.c_void_p(4096 + 512), C.c_void_p(1 << 21),
+                                  None) == af.AF_E_INVALID_ARG
+    assert "overlaps" in af._lib.af_last_error().decode()
