@@ -66,6 +66,8 @@ def _load():
         "af_transformer_forward_taps": (I, [P, P, P, P, I, P, I, I, I, I, I, P, P]),
         "af_flow_euler_cfg_step": (I, [P, P, I, I, I, I, F, F, F, P]),
         "af_flow_cfg_inputs": (I, [P, I, I, I, I, F, I, P, P, P]),
+        "af_attention_workspace_size": (SZ, [I, I, I, I]),
+        "af_attention": (I, [P, P, P, P, I, I, I, I, F, P, P, SZ, P]),
         "af_sigma_schedule": (I, [I, D, C.POINTER(F)]),
         "af_destroy": (V, [P]),
         "af_status_string": (C.c_char_p, [I]),
@@ -91,7 +93,8 @@ _lib = _load()
 EXPORTED = (
     "af_config_default", "af_check_shapes", "af_weight_count", "af_weight_info", "af_create",
     "af_load_weights", "af_init_weights", "af_transformer_forward", "af_transformer_forward_taps",
-    "af_flow_euler_cfg_step", "af_flow_cfg_inputs", "af_sigma_schedule", "af_destroy", "af_status_string",
+    "af_flow_euler_cfg_step", "af_flow_cfg_inputs", "af_attention_workspace_size", "af_attention",
+    "af_sigma_schedule", "af_destroy", "af_status_string",
     "af_last_error", "af_umt5_config_default", "af_umt5_weight_count", "af_umt5_weight_info",
     "af_umt5_create", "af_umt5_load_weights", "af_umt5_encode", "af_umt5_encode_taps", "af_umt5_destroy")
 
@@ -189,6 +192,51 @@ def af_flow_cfg_inputs(latents, sigma: float, cfg_on: bool, x_in, tau, stream=No
         _on_device(t, name, latents.device.index)
     _check(_lib.af_flow_cfg_inputs(C.c_void_p(latents.data_ptr()), Bi, Cc, H, W, sigma, 1 if cfg_on else 0,
                                    C.c_void_p(x_in.data_ptr()), C.c_void_p(tau.data_ptr()), _stream_ptr(stream)))
+
+
+def af_attention_workspace_size(B: int, S: int, H: int, head_dim: int = 256) -> int:
+    return int(_lib.af_attention_workspace_size(B, S, H, head_dim))
+
+
+def _attention_args(q, k, v, key_mask, num_heads, out):
+    import torch
+    _need(q.dim() == 3 and q.shape == k.shape == v.shape, "q, k, v must be [B, S, H * head_dim] of one shape")
+    _need(all(t.dtype == torch.bfloat16 and t.is_contiguous() for t in (q, k, v)),
+          "q, k, v must be contiguous bfloat16")
+    B, S, D = q.shape
+    _need(num_heads > 0 and D % num_heads == 0, "H * head_dim must equal the last dimension")
+    if key_mask is not None:
+        _need(key_mask.dtype == torch.uint8 and key_mask.is_contiguous() and tuple(key_mask.shape) == (B, S),
+              "key_mask must be contiguous uint8 [B, S]")
+    if out is not None:
+        _need(out.dtype == torch.bfloat16 and out.is_contiguous() and out.shape == q.shape,
+              "out must be contiguous bfloat16 of q's shape")
+    _on_device(q, "q", None)
+    for t, name in ((k, "k"), (v, "v"), (key_mask, "key_mask"), (out, "out")):
+        if t is not None:
+            _on_device(t, name, q.device.index)
+    return B, S, D // num_heads
+
+
+def af_attention(q, k, v, key_mask=None, num_heads: int = 12, eps: float = 1e-6, out=None, workspace=None,
+                 stream=None):
+    """QK-norm + joint attention on token-major bf16 q, k, v [B, S, H * 256] -> out of
+    the same shape. `workspace` (a uint8 device tensor) is allocated here when not
+    given."""
+    import torch
+    B, S, hd = _attention_args(q, k, v, key_mask, num_heads, out)
+    if out is None:
+        out = torch.empty_like(q)
+    need = af_attention_workspace_size(B, S, num_heads, hd)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _need(workspace.dtype == torch.uint8 and workspace.is_contiguous(), "workspace must be a contiguous uint8 tensor")
+    _on_device(workspace, "workspace", q.device.index)
+    mptr = C.c_void_p(key_mask.data_ptr()) if key_mask is not None else None
+    _check(_lib.af_attention(C.c_void_p(q.data_ptr()), C.c_void_p(k.data_ptr()), C.c_void_p(v.data_ptr()), mptr,
+                             B, S, num_heads, hd, eps, C.c_void_p(out.data_ptr()),
+                             C.c_void_p(workspace.data_ptr()), workspace.numel(), _stream_ptr(stream)))
+    return out
 
 
 def _stream_ptr(stream=None):

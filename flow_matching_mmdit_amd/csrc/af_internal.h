@@ -66,13 +66,15 @@ hipError_t gemm_f32(const GemmLaunch& L, hipStream_t s);
 // q.k/16 to [-16, 16]); the fp32 kernel takes plain q and KEY_KEEP = 0.
 constexpr float ATTN_BF16_Q_SCALE = 1.4426950408889634f / 16.0f;
 constexpr float ATTN_BF16_KEY_KEEP = -16.25f * 1.4426950408889634f;
-// part: scratch for split query tiles, attention_bf16_part_floats(n_cu) floats
-// (NULL: no splitting); n_cu: compute units of the device. o8 != NULL: the output
+// part: scratch for split query tiles, room for part_pieces pieces of
+// attention_bf16_part_floats(1) floats each (NULL: no splitting; at most n_cu
+// pieces are used); n_cu: compute units of the device. o8 != NULL: the output
 // goes to o8 [M, d] as MXFP8 with scales o8s [d/64][sc_rows][2] instead of o.
+// A query whose keys are all excluded gets a zero output.
 hipError_t attention_bf16(const bf16_t* q, const bf16_t* k, const bf16_t* vt, const float* bias,
-                          RowGeom g, int H, int S_pad, bf16_t* o, int d, int n_cu, float* part, uint8_t* o8,
-                          uint8_t* o8s, long sc_rows, hipStream_t s);
-size_t attention_bf16_part_floats(int n_cu);
+                          RowGeom g, int H, int S_pad, bf16_t* o, int d, int n_cu, float* part, int part_pieces,
+                          uint8_t* o8, uint8_t* o8s, long sc_rows, hipStream_t s);
+size_t attention_bf16_part_floats(int pieces);
 hipError_t attention_f32(const float* q, const float* k, const float* v, const float* bias,
                          RowGeom g, int H, int hd, int S_pad, float* o, int d, hipStream_t s);
 

@@ -541,7 +541,7 @@ af_status run_block(af_model* m, const View& V, RowGeom g, int S_pad, const Bloc
     ProfScope ps(m, AF_K_ATTENTION, s);
     if (m->dt == AF_BF16)
         AF_K(attention_bf16((const bf16_t*)V.q, (const bf16_t*)V.k, (const bf16_t*)V.v, V.kbias, g, D.H, S_pad,
-                            (bf16_t*)V.attn, d, m->n_cu, m->attn_part, V.attn8, V.attn_s, m->Mp, s));
+                            (bf16_t*)V.attn, d, m->n_cu, m->attn_part, m->n_cu, V.attn8, V.attn_s, m->Mp, s));
     else
         AF_K(attention_f32((const float*)V.q, (const float*)V.k, (const float*)V.v, V.kbias, g, D.H, D.hd, S_pad,
                            (float*)V.attn, d, s));

@@ -332,8 +332,8 @@ void k_attention_bf16(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K
         if (grp == 0) blk[QT * HD + ql] = l_tot;
         return;
     }
-    // ---- normalise and store
-    const float inv = 1.f / l_tot;
+    // ---- normalise and store (a query whose keys are all excluded gets zeros)
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     const int q = q0 + l32;
     if (O8) {
         // MXFP8 output: head-dim block ht (32 values) is held by lanes l and l ^ 32
@@ -395,7 +395,7 @@ __global__ __launch_bounds__(256) void k_attention_combine(const float* __restri
         acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
         l += blk[QT * HD + ql];
     }
-    const float inv = 1.f / l;
+    const float inv = l > 0.f ? 1.f / l : 0.f;
     const long row = g.row_of(b, q);
     if (O8) {
         // MXFP8 output: one 32-value block = 8 consecutive lanes
@@ -420,8 +420,8 @@ __global__ __launch_bounds__(256) void k_attention_combine(const float* __restri
 size_t attention_bf16_part_floats(int n_cu) { return (size_t)n_cu * (QT * HD + QT); }
 
 hipError_t attention_bf16(const bf16_t* q, const bf16_t* k, const bf16_t* vt, const float* bias, RowGeom g, int H,
-                          int S_pad, bf16_t* o, int d, int n_cu, float* part, uint8_t* o8, uint8_t* o8s,
-                          long sc_rows, hipStream_t s) {
+                          int S_pad, bf16_t* o, int d, int n_cu, float* part, int part_pieces, uint8_t* o8,
+                          uint8_t* o8s, long sc_rows, hipStream_t s) {
     const int S = g.S();
     if (g.B == 0 || S == 0) return hipSuccess;
     const int nqt = (S + QT - 1) / QT, ntiles = (S + KT - 1) / KT;
@@ -431,7 +431,7 @@ hipError_t attention_bf16(const bf16_t* q, const bf16_t* k, const bf16_t* vt, co
     // split into kp key ranges each (kp * tail <= n_cu, at least two key tiles
     // per piece) so the partial round is kp times shorter.
     int tail = part && n_cu > 0 ? total % n_cu : 0;
-    int kp = tail ? min(n_cu / tail, ntiles / 2) : 1;
+    int kp = tail ? min(min(n_cu, part_pieces) / tail, ntiles / 2) : 1;
     if (kp < 2) tail = 0, kp = 1;
     const int nfull = total - tail;
     hipLaunchKernelGGL(k_attention_bf16, dim3(nfull + tail * kp), dim3(256), 0, s, q, k, vt, bias, g, H, S_pad, o, d,

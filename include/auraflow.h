@@ -180,6 +180,39 @@ af_status af_transformer_forward_taps(af_model* m, const float* latents, const f
                                       int stop_after_block, float* residual_out, void* stream);
 
 /*
+ * The attention step of a block on its own ([TRANS] 注意力处理器与 QKV 融合:
+ * QK-norm, then one scaled-dot-product attention over the whole sequence,
+ * scale 1/sqrt(head_dim), no dropout, not causal), as the transformer forward
+ * computes it, for callers that hold their own projections:
+ *   q, k, v     device bf16 [B, S, H * head_dim], token-major (head h in
+ *               columns [h * head_dim, (h + 1) * head_dim)): the raw q, k, v
+ *               projections. q and k are layer-normalised over each head's
+ *               head_dim values (fp32 statistics, biased variance, `eps`, no
+ *               affine) before the product.
+ *   key_mask    device uint8 [B, S]; key j of sample b is excluded iff
+ *               key_mask[b * S + j] == 0. NULL = every key valid. A query whose
+ *               keys are all excluded gets a zero output.
+ *   out         device bf16 [B, S, H * head_dim], same layout as q; must not
+ *               overlap the inputs or the workspace.
+ *   workspace   device memory of at least
+ *               af_attention_workspace_size(B, S, H, head_dim) bytes, owned by
+ *               the caller; its prior content does not matter and it holds
+ *               scratch values after the call. A smaller workspace of at least
+ *               the size for an unsplit launch is accepted and only limits how
+ *               many query tiles of the last partial round are split over key
+ *               ranges (the result differs from the split one by fp32 summation
+ *               order only).
+ * Requires head_dim == 256 (else AF_E_UNSUPPORTED) and S <= 2^20. B, S or H
+ * equal to 0 is a no-op. The launches (QK-norm pack, v transpose and key bias,
+ * attention, combine) are enqueued on `stream`; nothing is allocated.
+ * af_attention_workspace_size returns 0 for invalid sizes.
+ */
+size_t af_attention_workspace_size(int B, int S, int H, int head_dim);
+af_status af_attention(const void* q, const void* k, const void* v, const uint8_t* key_mask, int B, int S,
+                       int H, int head_dim, float eps, void* out, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/*
  * Flow-matching Euler step with classifier-free guidance ([PIPE] section
  * AuraFlowPipeline 核心参数详解: uncond + s (text - uncond), off for s <= 1;
  * [TRANS] 在 AuraFlowPipeline 中的实际调用: outputs split as (uncond, text)):
