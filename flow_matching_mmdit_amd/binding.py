@@ -68,6 +68,8 @@ def _load():
         "af_flow_cfg_inputs": (I, [P, I, I, I, I, F, I, P, P, P]),
         "af_attention_workspace_size": (SZ, [I, I, I, I]),
         "af_attention": (I, [P, P, P, P, I, I, I, I, F, P, P, SZ, P]),
+        "af_attention_noalloc": (I, [P, P, P, P, I, I, I, I, F, P, P]),
+        "af_attention_noalloc_max_bytes": (SZ, []),
         "af_sigma_schedule": (I, [I, D, C.POINTER(F)]),
         "af_destroy": (V, [P]),
         "af_status_string": (C.c_char_p, [I]),
@@ -94,6 +96,7 @@ EXPORTED = (
     "af_config_default", "af_check_shapes", "af_weight_count", "af_weight_info", "af_create",
     "af_load_weights", "af_init_weights", "af_transformer_forward", "af_transformer_forward_taps",
     "af_flow_euler_cfg_step", "af_flow_cfg_inputs", "af_attention_workspace_size", "af_attention",
+    "af_attention_noalloc", "af_attention_noalloc_max_bytes",
     "af_sigma_schedule", "af_destroy", "af_status_string",
     "af_last_error", "af_umt5_config_default", "af_umt5_weight_count", "af_umt5_weight_info",
     "af_umt5_create", "af_umt5_load_weights", "af_umt5_encode", "af_umt5_encode_taps", "af_umt5_destroy")
@@ -237,6 +240,23 @@ def af_attention(q, k, v, key_mask=None, num_heads: int = 12, eps: float = 1e-6,
                              B, S, num_heads, hd, eps, C.c_void_p(out.data_ptr()),
                              C.c_void_p(workspace.data_ptr()), workspace.numel(), _stream_ptr(stream)))
     return out
+
+
+def af_attention_noalloc(q, k, v, key_mask=None, num_heads: int = 12, eps: float = 1e-6, out=None, stream=None):
+    """af_attention with the library's fixed per-device scratch: the call itself
+    allocates nothing on the device (pass `out` to allocate nothing here either)."""
+    import torch
+    B, S, hd = _attention_args(q, k, v, key_mask, num_heads, out)
+    if out is None:
+        out = torch.empty_like(q)
+    mptr = C.c_void_p(key_mask.data_ptr()) if key_mask is not None else None
+    _check(_lib.af_attention_noalloc(C.c_void_p(q.data_ptr()), C.c_void_p(k.data_ptr()), C.c_void_p(v.data_ptr()),
+                                     mptr, B, S, num_heads, hd, eps, C.c_void_p(out.data_ptr()), _stream_ptr(stream)))
+    return out
+
+
+def af_attention_noalloc_max_bytes() -> int:
+    return int(_lib.af_attention_noalloc_max_bytes())
 
 
 def _stream_ptr(stream=None):

@@ -13,6 +13,7 @@
 // call, so a workspace of any prior content is valid.
 #include <algorithm>
 #include <cstdio>
+#include <mutex>
 
 #include "af_internal.h"
 
@@ -123,6 +124,36 @@ __global__ __launch_bounds__(256) void k_attn_pack_vt(const bf16_t* __restrict__
     }
 }
 
+// Scratch of af_attention_noalloc: one fixed array per device, in the code
+// object (each GPU the library runs on holds its own copy until the process
+// ends). Host code never passes `scratch` itself to a kernel (in host code the
+// name is a host-side stand-in, not a device address): its device address is
+// looked up once per device with hipGetSymbolAddress and kept in g_scratch.
+constexpr size_t NOALLOC_BYTES = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[NOALLOC_BYTES];
+constexpr int MAX_DEV = 64;
+void* g_scratch[MAX_DEV] = {};
+std::mutex g_scratch_mu;
+
+int device_cus();
+
+// The current device's scratch address (looked up on the first call on it).
+af_status scratch_ptr(char** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return report(AF_E_HIP, hipGetErrorString(e));
+    if (dev < 0 || dev >= MAX_DEV) return report(AF_E_UNSUPPORTED, "device index beyond the scratch table");
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) return report(AF_E_HIP, "hipGetSymbolAddress of the attention scratch failed");
+        g_scratch[dev] = p;
+    }
+    *out = (char*)g_scratch[dev];
+    return AF_OK;
+}
+
 int device_cus() {
     static int cache[64] = {};
     int dev = 0;
@@ -194,5 +225,27 @@ af_status af_attention(const void* q, const void* k, const void* v, const uint8_
     return run_attn((const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, key_mask, B, S, H, eps, (bf16_t*)out,
                     (char*)workspace, pieces, (hipStream_t)stream);
 }
+
+af_status af_attention_noalloc(const void* q, const void* k, const void* v, const uint8_t* key_mask, int B, int S,
+                               int H, int head_dim, float eps, void* out, void* stream) {
+    af_status st = check_attn(q, k, v, B, S, H, head_dim, eps, out);
+    if (st != AF_OK || (long)B * S * H == 0) return st;
+    const AttnWs base = attn_ws(B, S, H, 0);
+    if (base.total > NOALLOC_BYTES) {
+        char msg[200];
+        snprintf(msg, sizeof msg, "af_attention_noalloc: B * H * S needs %zu bytes of scratch; the fixed scratch holds %zu "
+                 "(use af_attention with a workspace)", base.total, NOALLOC_BYTES);
+        return report(AF_E_SHAPE, msg);
+    }
+    char* ws = nullptr;
+    st = scratch_ptr(&ws);
+    if (st != AF_OK) return st;
+    const size_t per = attention_bf16_part_floats(1) * 4;
+    const int pieces = (int)std::min<size_t>((NOALLOC_BYTES - base.total) / per, (size_t)std::max(device_cus(), 0));
+    return run_attn((const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, key_mask, B, S, H, eps, (bf16_t*)out, ws,
+                    pieces, (hipStream_t)stream);
+}
+
+size_t af_attention_noalloc_max_bytes(void) { return NOALLOC_BYTES; }
 
 }  // extern "C"

@@ -213,6 +213,31 @@ af_status af_attention(const void* q, const void* k, const void* v, const uint8_
                        void* stream);
 
 /*
+ * af_attention without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same arguments and result as af_attention, with
+ * the scratch taken from a fixed array of af_attention_noalloc_max_bytes()
+ * (64 MiB) that the library holds on every device it runs on until the process
+ * ends. Nothing is allocated or freed by the call. The device is the calling
+ * thread's current HIP device (the one `stream` belongs to).
+ * Limit: the packed operands and key bias, 3 * B * H * S_pad * 512 + B * S_pad * 4
+ * bytes rounded up per part (S_pad = S rounded up to 128), must fit the 64 MiB
+ * (for example B = 2, H = 12, S <= 1792); larger calls return AF_E_SHAPE before
+ * anything is enqueued. Whatever room is left holds the partial sums of split
+ * query tiles (up to one piece per compute unit), so a call near the limit
+ * splits fewer tiles than af_attention would (results then differ from it by
+ * fp32 summation order only).
+ * Every call on a device shares that device's scratch and leaves its own
+ * intermediate values in it; each call writes everything it later reads, so
+ * nothing needs clearing between calls. Calls that overlap in time on one device
+ * (on different streams, or from different threads) race on the scratch and
+ * must be serialised by the caller.
+ */
+af_status af_attention_noalloc(const void* q, const void* k, const void* v, const uint8_t* key_mask, int B,
+                               int S, int H, int head_dim, float eps, void* out, void* stream);
+size_t af_attention_noalloc_max_bytes(void);
+
+/*
  * Flow-matching Euler step with classifier-free guidance ([PIPE] section
  * AuraFlowPipeline 核心参数详解: uncond + s (text - uncond), off for s <= 1;
  * [TRANS] 在 AuraFlowPipeline 中的实际调用: outputs split as (uncond, text)):
