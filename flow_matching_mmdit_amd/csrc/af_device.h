@@ -45,15 +45,17 @@ __device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float 
     return (uint32_t)w;
 }
 
-// x * sigmoid(x) with the hardware exponential and a fast (not IEEE-rounded) division.
-__device__ __forceinline__ float silu_f(float x) { return __fdividef(x, 1.0f + __expf(-x)); }
+// x * sigmoid(x) with the hardware exponential and reciprocal (v_exp_f32,
+// v_rcp_f32: about 1 ulp each; __fdividef compiles to the full IEEE division
+// sequence here, about ten VALU instructions per element).
+__device__ __forceinline__ float silu_f(float x) { return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 
 // GELU in its tanh form, 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))), written
 // as x * sigmoid(2 sqrt(2/pi) (x + 0.044715 x^3)) (the same function: 0.5 (1 + tanh z)
 // = sigmoid(2 z)).
 __device__ __forceinline__ float gelu_tanh_f(float x) {
     const float z = 1.5957691216057308f * (x + 0.044715f * x * x * x);
-    return __fdividef(x, 1.f + __expf(-z));
+    return x * __builtin_amdgcn_rcpf(1.f + __expf(-z));
 }
 
 // Lane reductions through DPP (row-local VALU operand swizzles) rather than

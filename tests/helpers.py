@@ -78,11 +78,42 @@ class PrefetchWeights:
         return name.rsplit(".", 1)[0] if "." in name else "_embed"
 
     def __getitem__(self, name):
-        if name not in self._cache:
-            grp = self._group(name)
+        # the two most recent groups stay cached (a joint block's two streams)
+        grp = self._group(name)
+        if grp not in self._cache:
             names = [n for n, _, _ in self._specs if self._group(n) == grp]
-            self._cache = dict(zip(names, self._pool.map(lambda n: self._base[n], names)))
-        return self._cache[name]
+            if len(self._cache) >= 2:
+                self._cache.pop(next(iter(self._cache)))
+            self._cache[grp] = dict(zip(names, self._pool.map(lambda n: self._base[n], names)))
+        return self._cache[grp][name]
 
     def as_weights(self):
         return oracle.Weights(self.cfg, self.__getitem__)
+
+
+BLOCK_KEYS = ("ada", "wq", "wk", "wv", "wo", "ff1", "ff2", "ff3")
+
+
+def block_weights(W, prefix):
+    return {k: W[prefix + k] for k in BLOCK_KEYS}
+
+
+def oracle_block_on(ocfg, W, temb, kv, x_prev, b, Nt, mx=False):
+    """The oracle's block b (0-based over the joint, then the single blocks) applied
+    to the residual x_prev [B, S, d] (rows [registers, text, image] per sample;
+    the first Nt rows are the text stream)."""
+    x_prev = np.asarray(x_prev, np.float32)
+    if b < ocfg.num_mmdit_layers:
+        xt, xi = oracle.joint_block(ocfg, block_weights(W, f"joint{b}.img."), block_weights(W, f"joint{b}.txt."),
+                                    temb, x_prev[:, :Nt], x_prev[:, Nt:], kv, np.float32, mx)
+        return np.concatenate([xt, xi], 1)
+    return oracle.single_block(ocfg, block_weights(W, f"single{b - ocfg.num_mmdit_layers}."), temb, x_prev, kv,
+                               np.float32, mx)
+
+
+def update_metrics(got_prev, got, ref_next):
+    """A block's own update: the GPU's (got - got_prev) against the oracle's update of
+    the same input residual (ref_next - got_prev); returns (max|d|/max|ref|, cosine)."""
+    dg = np.asarray(got, np.float64) - got_prev
+    dr = np.asarray(ref_next, np.float64) - got_prev
+    return rel_max(dg, dr), cosine(dg, dr)

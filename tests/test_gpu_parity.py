@@ -10,7 +10,7 @@ import pytest
 
 import oracle
 import seeded_inputs
-from helpers import cosine, oracle_cfg, rel_max, to_dev, workload_inputs
+from helpers import cosine, oracle_block_on, oracle_cfg, rel_max, to_dev, update_metrics, workload_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -146,16 +146,22 @@ def small_bf16(af):
 
 def test_small_bf16_blocks_match_oracle(af, small_bf16):
     torch = _torch()
-    cfg, m, dev, ref, taps, _ = small_bf16
+    cfg, m, dev, ref, taps, host = small_bf16
     got = {blk: m.forward_taps(*dev, stop_after_block=blk).cpu().numpy() for blk in (-1, 0, 1, 2)}
     out = m.forward(*dev).cpu().numpy()
     torch.cuda.synchronize()
     assert rel_max(got[-1], taps[-1]) <= 1e-2
+    ocfg = oracle_cfg(cfg)
+    W_o = oracle.Weights.seeded(ocfg, seed=0, bf16=True)
+    temb, xt, _, kv = oracle.embed(ocfg, W_o, *host, np.float32)
     for blk in (0, 1, 2):
         e, c = rel_max(got[blk], taps[blk]), cosine(got[blk], taps[blk])
         assert e <= BF16_TOL and c >= BF16_COS, (blk, e, c)
-        dg, dr = got[blk] - got[blk - 1], taps[blk] - taps[blk - 1]
-        assert cosine(dg, dr) >= 0.99, (blk, cosine(dg, dr))
+        # the block's own update: the oracle's block applied to the GPU's input residual
+        eu, cu = update_metrics(got[blk - 1], got[blk],
+                                oracle_block_on(ocfg, W_o, temb, kv, got[blk - 1], blk, xt.shape[1]))
+        print(f"block {blk}: rel {e:.3e} cos {c:.6f}; update rel {eu:.3e} cos {cu:.6f}")
+        assert eu <= BF16_TOL and cu >= BF16_COS, (blk, eu, cu)
     e, c = rel_max(out, ref), cosine(out, ref)
     assert e <= BF16_TOL and c >= BF16_COS, (e, c)
 
@@ -306,13 +312,18 @@ def test_block_pair_bf16_matches_oracle(af, block_pair):
     got = {blk: m.forward_taps(*dev, stop_after_block=blk).cpu().numpy() for blk in (-1, 0, 1)}
     out = m.forward(*dev).cpu().numpy()
     torch.cuda.synchronize()
+    temb, xt, _, kv = oracle.embed(ocfg, W_o, lat, taus, text, mask, np.float32)
     for blk in (0, 1):
         assert np.isfinite(taps[blk]).all()
         bad = np.argwhere(~np.isfinite(got[blk]))
         assert len(bad) == 0, (blk, len(bad), bad[:8].tolist())
         e, c = rel_max(got[blk], taps[blk]), cosine(got[blk], taps[blk])
-        print(f"block {blk}: rel {e:.3e} cos {c:.6f}")
+        # the block's own update: the oracle's block on the GPU's input residual
+        eu, cu = update_metrics(got[blk - 1], got[blk],
+                                oracle_block_on(ocfg, W_o, temb, kv, got[blk - 1], blk, xt.shape[1]))
+        print(f"block {blk}: rel {e:.3e} cos {c:.6f}; update rel {eu:.3e} cos {cu:.6f}")
         assert e <= BF16_TOL and c >= BF16_COS, (blk, e, c)
+        assert eu <= BF16_TOL and cu >= BF16_COS, (blk, eu, cu)
     e, c = rel_max(out, ref), cosine(out, ref)
     print(f"output: rel {e:.3e} cos {c:.6f}")
     assert e <= BF16_TOL and c >= BF16_COS, (e, c)
