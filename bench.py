@@ -159,9 +159,58 @@ def cpu_baseline(shape, threads):
         "value": 1.0 / t_fwd, "unit": "forwards/s", "cores": threads, "kind": "oracle",
         "sample": (f"numpy fp32 oracle, BLAS threads={threads}: embedding ({t_embed:.2f} s) + 1 joint block "
                    f"({t_joint:.2f} s) + 1 single block ({t_single:.2f} s) at the full {8 * W}x{8 * H}-pixel CFG-batch-2 "
-                   f"shape; forward extrapolated as embed + 4 joint + 32 single = {t_fwd:.1f} s; weight "
-                   f"generation ({gen_s:.1f} s) excluded"),
+                   f"shape; forward extrapolated as embed + 4 joint + 32 single = {t_fwd:.1f} s (extrapolated, not a "
+                   f"timed full forward); weight generation ({gen_s:.1f} s) excluded"),
+        "blas": blas_vendor(),
+        "full_forwards": oracle_full_forwards(),
     }
+
+
+def blas_vendor():
+    """The BLAS library numpy was built against (name and version as numpy reports them)."""
+    try:
+        dep = np.__config__.CONFIG["Build Dependencies"]["blas"]
+        return f"{dep.get('name')} {dep.get('version')}"
+    except Exception:
+        return "unknown"
+
+
+def oracle_full_forwards():
+    """Timed whole oracle forwards (fp32 numpy) of the two small workloads: the tiny
+    fp32 transformer (1 joint + 1 single block, 4 heads x 8, latent 4x16x16, 8 text
+    tokens, batch 1, t = 500) and the full-width block pair (1 joint + 1 single block,
+    d = 3072, latent 4x64x64, 256 text tokens, CFG batch 2). Weight generation and
+    bf16 rounding are excluded."""
+    import oracle
+    import seeded_inputs
+    from dataclasses import replace
+    out = {}
+    cases = {
+        "tiny_fp32": (replace(oracle.TINY), 1, 16, 8, False),
+        "block_pair_512": (replace(oracle.FULL, num_mmdit_layers=1, num_single_dit_layers=1), 2, 64, 256, True),
+    }
+    for name, (cfg, B, lat_hw, T, bf16) in cases.items():
+        W_ = oracle.Weights.seeded(cfg, seed=0, bf16=bf16)
+        W_ = oracle.Weights.from_dict(cfg, {n: W_[n] for n, _, _ in oracle.weight_specs(cfg)})
+        if B == 2:
+            lat = np.concatenate([seeded_inputs.latents(1, 4, lat_hw, lat_hw)] * 2)
+            t = seeded_inputs.timesteps_uniform(1) / 1000.0
+            tau = np.concatenate([t, t]).astype(np.float32)
+            mask = seeded_inputs.length_mask(seeded_inputs.valid_lengths(B, 16, T), T)
+        else:
+            lat = seeded_inputs.latents(1, 4, lat_hw, lat_hw)
+            tau = np.array([0.5], np.float32)
+            mask = None
+        text = seeded_inputs.text_embeddings(B, T, cfg.joint_attention_dim)
+        if bf16:
+            text = oracle.round_bf16(text)
+        t0 = time.time()
+        oracle.forward(cfg, W_, lat, tau, text, mask, np.float32)
+        dt = time.time() - t0
+        out[name] = {"s_per_forward": dt, "value": 1.0 / dt, "unit": "forwards/s",
+                     "config": f"{cfg.num_mmdit_layers} joint + {cfg.num_single_dit_layers} single blocks, "
+                               f"d={cfg.inner_dim}, latent 4x{lat_hw}x{lat_hw}, {T} text tokens, batch {B}"}
+    return out
 
 
 def text_encoder_leg(args, af, torch, steps, warmup):
@@ -201,21 +250,93 @@ def text_encoder_leg(args, af, torch, steps, warmup):
 
 
 def sampling_loop_bench(args, af, torch):
-    """25 Euler steps (shift 1.73, guidance 3.5) for 4 images at 1024^2: each step is one
-    transformer forward over [4 uncond; 4 cond] and one CFG + Euler update. Wall time per
-    loop from HIP events around whole loops (sigma schedule computed on the host inside)."""
-    import seeded_inputs
-    imgs, H, W, T, steps = 4, 128, 128, 256, 25
+    """--sampling-loop: the 25-step CFG loop for 4 images at 1024^2 (transformer batch 8)
+    as its own JSON line; --steps counts loops."""
+    imgs, H, W, T = 4, 128, 128, 256
     B = 2 * imgs
     cfg = af.make_config(max_batch=B, max_latent_h=H, max_latent_w=W, max_text_len=T,
                          compute_dtype=af.AF_MXFP8 if args.mxfp8 else af.AF_BF16)
+    model = af.AuraFlowModel(cfg, 0)
+    model.load_seeded_weights(seed=0, threads=_cpu_threads())
+    leg = loop_leg(af, torch, model, cfg, args.steps, args.warmup, imgs, H, W, T)
+    print(json.dumps({
+        "metric": "25-step CFG sampling loop, 4 images at 1024² (transformer batch 8)",
+        "value": leg["value"], "unit": "images/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": leg["ms_per_loop"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "mxfp8+bf16" if args.mxfp8 else "bf16", "data": "synthetic",
+        "config": {"workload": leg["workload"] + "; a step is one whole 25-step loop",
+                   "global_batch": B, "seq_len": cfg.num_register_tokens + T + (H // 2) * (W // 2),
+                   "parallelism": "single GPU"},
+        "tflops": leg["tflops"], "pct_peak_bf16": leg["pct_peak_bf16"],
+    }))
+    model.close()
+
+
+def workload_tensors(torch, af_cfg, B, H, W, T):
+    """The bench's seeded inputs: CFG pairs sharing one latent and timestep,
+    independent text rows, seeded valid lengths with the padding masked."""
+    import seeded_inputs
+    lat1 = seeded_inputs.latents(B // 2, 4, H, W)
+    lat = torch.from_numpy(np.concatenate([lat1, lat1])).cuda()
+    t = seeded_inputs.timesteps_uniform(B // 2) / 1000.0
+    tau = torch.from_numpy(np.concatenate([t, t]).astype(np.float32)).cuda()
+    text = torch.from_numpy(seeded_inputs.text_embeddings(B, T, af_cfg.joint_attention_dim)).cuda()
+    mask = torch.from_numpy(seeded_inputs.length_mask(seeded_inputs.valid_lengths(B, 16, T), T)).cuda()
+    return lat, tau, text, mask
+
+
+def forward_leg(af, torch, model, cfg, B, H, W, T, steps, warmup):
+    """Forwards/s, TFLOP/s and the attention roofline of one more workload on an
+    existing model (timed as the headline: HIP events on the forward's stream)."""
     d = cfg.num_attention_heads * cfg.attention_head_dim
     F = ((8 * d) // 3 + 255) // 256 * 256
     L = cfg.num_mmdit_layers + cfg.num_single_dit_layers
     Nimg = (H // 2) * (W // 2)
     S = cfg.num_register_tokens + T + Nimg
-    model = af.AuraFlowModel(cfg, 0)
-    model.load_seeded_weights(seed=0, threads=_cpu_threads())
+    lat, tau, text, mask = workload_tensors(torch, cfg, B, H, W, T)
+    out = torch.empty((B, 4, H, W), dtype=torch.float32, device="cuda")
+    for _ in range(warmup):
+        model.forward(lat, tau, text, mask, out=out)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out).all()), f"non-finite output at {8 * W}x{8 * H}"
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        model.forward(lat, tau, text, mask, out=out)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    af.af_profile(model, True)
+    for _ in range(steps):
+        model.forward(lat, tau, text, mask, out=out)
+    torch.cuda.synchronize()
+    prof = af.af_profile_read(model)
+    af.af_profile(model, False)
+    kms, n = prof["attention"]
+    work, _ = class_work("attention", d, F, B, S)
+    att = work / (kms / n * 1e-3) / 1e12
+    flops = forward_flops(d, F, L, B, S, T, cfg.joint_attention_dim, Nimg, 16)
+    return {"workload": f"AuraFlow transformer forward at {8 * W}x{8 * H} pixels (latent 4x{H}x{W}: {Nimg} image + "
+                        f"8 register + {T} text tokens, sequence {S}), CFG batch {B}, same model and recipe",
+            "ms_per_step": ms, "value": 1000.0 / ms, "unit": "forwards/s", "steps": steps, "warmup": warmup,
+            "flops_per_forward": flops, "tflops": flops / (ms * 1e-3) / 1e12,
+            "pct_peak_bf16": 100.0 * flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "attention": {"avg_launch_ms": kms / n, "launches_per_forward": n / steps, "work_per_launch": work,
+                          "tflops": att, "peak": PEAK_BF16_TFLOPS, "frac_peak": att / PEAK_BF16_TFLOPS}}
+
+
+def loop_leg(af, torch, model, cfg, loops, warmup_loops, imgs=4, H=128, W=128, T=256, steps=25):
+    """The 25-step flow-matching Euler + CFG loop (shift 1.73, guidance 3.5) for `imgs`
+    images at 1024^2 on an existing model: transformer batch 2 imgs per step. Wall
+    time per loop from HIP events around whole loops."""
+    import seeded_inputs
+    B = 2 * imgs
+    d = cfg.num_attention_heads * cfg.attention_head_dim
+    F = ((8 * d) // 3 + 255) // 256 * 256
+    L = cfg.num_mmdit_layers + cfg.num_single_dit_layers
+    Nimg = (H // 2) * (W // 2)
+    S = cfg.num_register_tokens + T + Nimg
     x0 = torch.from_numpy(seeded_inputs.latents(imgs, 4, H, W)).cuda()
     text = torch.from_numpy(seeded_inputs.text_embeddings(B, T, cfg.joint_attention_dim)).cuda()
     mask = torch.from_numpy(seeded_inputs.length_mask(seeded_inputs.valid_lengths(B, 16, T), T)).cuda()
@@ -226,34 +347,25 @@ def sampling_loop_bench(args, af, torch):
         x.copy_(x0)
         model.sample(x, text, mask, num_steps=steps, shift=1.73, guidance=3.5)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup_loops):
         loop()
     torch.cuda.synchronize()
     assert bool(torch.isfinite(x).all()), "non-finite latents after the warm-up loop"
-    print("[bench] sampling-loop warm-up done", file=sys.stderr, flush=True)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     e0.record(stream)
-    for _ in range(args.steps):
+    for _ in range(loops):
         loop()
     e1.record(stream)
     torch.cuda.synchronize()
     assert bool(torch.isfinite(x).all()), "non-finite latents after the timed loops"
-    ms = e0.elapsed_time(e1) / args.steps
+    ms = e0.elapsed_time(e1) / loops
     flops = steps * forward_flops(d, F, L, B, S, T, cfg.joint_attention_dim, Nimg, 16)
-    print(json.dumps({
-        "metric": "25-step CFG sampling loop, 4 images at 1024² (transformer batch 8)",
-        "value": imgs * 1000.0 / ms, "unit": "images/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "mxfp8+bf16" if args.mxfp8 else "bf16", "data": "synthetic",
-        "config": {"workload": "flow-matching Euler sampling, 25 steps, shift 1.73, guidance 3.5, 4 images "
-                               "at 1024x1024 (latent 4x128x128), [4 uncond; 4 cond] per forward, seeded random "
-                               "weights and text, padded text masked; a step is one whole 25-step loop",
-                   "global_batch": B, "seq_len": S, "parallelism": "single GPU"},
-        "tflops": flops / (ms * 1e-3) / 1e12,
-        "pct_peak_bf16": 100.0 * flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-    }))
-    model.close()
+    return {"workload": f"flow-matching Euler sampling, {steps} steps, shift 1.73, guidance 3.5, {imgs} images at "
+                        f"{8 * W}x{8 * H} (latent 4x{H}x{W}), [{imgs} uncond; {imgs} cond] per forward (transformer "
+                        f"batch {B}), seeded random weights and text, padded text masked",
+            "ms_per_loop": ms, "value": imgs * 1000.0 / ms, "unit": "images/s", "loops": loops,
+            "warmup_loops": warmup_loops, "flops_per_loop": flops, "tflops": flops / (ms * 1e-3) / 1e12,
+            "pct_peak_bf16": 100.0 * flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
 
 
 def main():
@@ -279,6 +391,8 @@ def main():
                     help="skip the text-encoder timing reported beside the transformer line")
     ap.add_argument("--no-graph-leg", action="store_true",
                     help="skip the graph-replay timing reported beside the eager line")
+    ap.add_argument("--no-extra-legs", action="store_true",
+                    help="skip the 1536^2 forward and the 25-step sampling loop reported beside the headline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run the plain 512 MiB device copy used to scale the HBM byte counters")
     args = ap.parse_args()
@@ -317,7 +431,11 @@ def main():
     B, H, W, T = WORKLOADS[args.workload]
     if args.latent:
         H, W = (int(x) for x in args.latent.lower().split("x"))
-    cfg = af.make_config(max_batch=B, max_latent_h=H, max_latent_w=W, max_text_len=T,
+    # the headline run also times 1536^2 and the batch-8 sampling loop on the same
+    # model, so its workspace is sized for both (the size does not change the kernels)
+    extra = not args.no_extra_legs and not args.mxfp8 and not args.latent and args.workload == "1024"
+    cfg = af.make_config(max_batch=max(B, 8) if extra else B, max_latent_h=max(H, 192) if extra else H,
+                         max_latent_w=max(W, 192) if extra else W, max_text_len=T,
                          compute_dtype=af.AF_MXFP8 if args.mxfp8 else af.AF_BF16)
     d = cfg.num_attention_heads * cfg.attention_head_dim
     F = ((8 * d) // 3 + 255) // 256 * 256
@@ -333,12 +451,7 @@ def main():
     print(f"[bench] weights ready in {setup_s:.1f} s", file=sys.stderr, flush=True)
 
     # Workload inputs: CFG pair sharing one latent and timestep, independent text, padded text masked.
-    lat1 = seeded_inputs.latents(B // 2, 4, H, W)
-    lat = torch.from_numpy(np.concatenate([lat1, lat1])).cuda()
-    t = seeded_inputs.timesteps_uniform(B // 2) / 1000.0
-    tau = torch.from_numpy(np.concatenate([t, t]).astype(np.float32)).cuda()
-    text = torch.from_numpy(seeded_inputs.text_embeddings(B, T, cfg.joint_attention_dim)).cuda()
-    mask = torch.from_numpy(seeded_inputs.length_mask(seeded_inputs.valid_lengths(B, 16, T), T)).cuda()
+    lat, tau, text, mask = workload_tensors(torch, cfg, B, H, W, T)
     out = torch.empty((B, 4, H, W), dtype=torch.float32, device="cuda")
 
     def check_finite(where):
@@ -450,6 +563,17 @@ def main():
                             "unit": "GB/s", "frac": work / avg / 1e9 / PEAK_HBM_GBS, "traffic": measured_traffic(name),
                             "avg_launch_ms": avg * 1e3, "work_per_launch": work}
 
+    # Beside the headline, on the same model: 1536^2 (the attention-dominated
+    # workload) and the 25-step sampling loop for 4 images (transformer batch 8).
+    d_leg = loop = None
+    if extra:
+        d_leg = forward_leg(af, torch, model, cfg, 2, 192, 192, T, min(args.steps, 10), 2)
+        print(f"[bench] 1536^2: {d_leg['ms_per_step']:.2f} ms/forward, attention "
+              f"{d_leg['attention']['avg_launch_ms']:.3f} ms/launch", file=sys.stderr, flush=True)
+        loop = loop_leg(af, torch, model, cfg, 1, 1)
+        print(f"[bench] sampling loop: {loop['ms_per_loop'] / 1000:.2f} s per 25-step loop of 4 images",
+              file=sys.stderr, flush=True)
+
     # Beside the bf16 line: the same workload on the MXFP8 model (QKV, out-projection
     # and FFN products on MXFP8 operands), timed the same way; reported as its own
     # object, never as `value`.
@@ -512,6 +636,8 @@ def main():
         "flops_per_forward": flops,
         "roofline": roofline,
         "graph_replay": graph_leg,
+        "config_1536": d_leg,
+        "sampling_loop": loop,
         "mxfp8_model": mx_leg,
         "text_encoder": te,
         "cpu_baseline": cpu,

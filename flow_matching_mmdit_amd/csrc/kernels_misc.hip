@@ -188,8 +188,8 @@ __global__ __launch_bounds__(256) void k_gemv_bf16(const float* __restrict__ x, 
 // Same summation order as k_gemv_bf16: results are bit-identical.
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
-template <int BC, int NI, int R>
-__global__ __launch_bounds__(256) void k_gemv_bf16_lds(const float* __restrict__ x, int B, int K,
+template <int BC, int NI, int R, int NT = 256>
+__global__ __launch_bounds__(NT) void k_gemv_bf16_lds(const float* __restrict__ x, int B, int K,
                                                        const bf16_t* __restrict__ W, int N,
                                                        const bf16_t* __restrict__ bias, int silu_in,
                                                        float* __restrict__ y, int b0) {
@@ -259,6 +259,20 @@ hipError_t gemv(const float* x, int B, int K, const void* W, af_dtype wdt, int N
     if (B == 0 || N == 0) return hipSuccess;
     constexpr int BC = 2;
     if (K > 4096) return hipErrorInvalidValue;
+    // K = 3072 with more than two samples: eight samples per pass over the
+    // weights (96 KB of inputs in LDS, one 512-thread workgroup per CU), so a
+    // batch of 8 streams the weights once. Each (row, sample) dot product is
+    // summed in the same order as in the two-sample instance: bit-identical.
+    if (wdt == AF_BF16 && K == 3072 && B > 2) {
+        constexpr int BC8 = 8, R = 4, NT = 512;
+        for (int b0 = 0; b0 < B; b0 += BC8) {
+            hipLaunchKernelGGL((k_gemv_bf16_lds<BC8, 6, R, NT>), dim3(min((N + 8 * R - 1) / (8 * R), 2048)), dim3(NT),
+                               0, s, x, B, K, (const bf16_t*)W, N, (const bf16_t*)bias, silu_in, y, b0);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+    }
     for (int b0 = 0; b0 < B; b0 += BC) {
         if (wdt == AF_BF16) {
             const int ni = (K + 511) / 512;
