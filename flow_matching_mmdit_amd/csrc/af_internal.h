@@ -16,8 +16,11 @@ enum GemmEpi {
     EPI_QKV = 3,            // bf16 only: per-head LayerNorm of q, k; q, k -> [B,H,S_pad,hd]; v -> v^T [B,H,hd,S_pad]
     EPI_SWIGLU = 4,         // bf16 only: h[m, f] = silu(acc[gate col]) * acc[up col], 32-column interleave
     EPI_GEGLU = 5,          // bf16 only: as SWIGLU with the tanh-form GELU in place of silu (text encoder)
-    EPI_PARTIAL = 6         // bf16 only, one group: split-K partial sums, C = fp32 [ksplit][M][N]; split s
+    EPI_PARTIAL = 6,        // bf16 only, one group: split-K partial sums, C = fp32 [ksplit][M][N]; split s
                             // covers K columns [s K/ksplit, (s+1) K/ksplit); splitk_resid adds them up
+    EPI_CONV = 7            // bf16 only, one group: C[m, n] = acc + cbias[n] (+ resid[m, n]), fp32 or bf16
+                            // (c_bf16), leading dim ldc for C and resid; with conv != 0 the A operand is the
+                            // implicit-GEMM gather of a 3x3 convolution (see conv below)
 };
 
 struct GemmGroup {
@@ -48,6 +51,17 @@ struct GemmLaunch {
     float q_scale;                     // QKV: factor on the normalised q before rounding (1 = none)
     int ksplit;                        // PARTIAL: number of K ranges (K a multiple of 32 ksplit)
     int n_cu;                          // compute units (0: always 256 x 256 tiles); N a multiple of 256
+                                       // (EPI_CONV: a multiple of 128; N % 256 != 0 runs 128 x 128 tiles)
+    // EPI_CONV
+    const float* cbias;                // [N] or NULL
+    int c_bf16;                        // 1: C is bf16, 0: fp32
+    // conv = 1: A[m, k] = X[b, y + dy, x + dx, c] for output pixel m = (b, y, x) of an
+    // cH x cW image, k = (3 (dy + 1) + dx + 1) cCin + c, X = g[0].A NHWC bf16 with cCin
+    // channels (a multiple of 32), zero outside the image (a 3x3 convolution with
+    // zero padding, K = 9 cCin); conv = 2: the same on the 2x nearest upsampling of a
+    // cH x cW input (the output image is 2cH x 2cW). a_bytes: bytes of X (< 2^31).
+    int conv, cH, cW, cCin;
+    long a_bytes;
 };
 
 hipError_t gemm_bf16(const GemmLaunch& L, hipStream_t s);
@@ -60,12 +74,16 @@ hipError_t gemm_f32(const GemmLaunch& L, hipStream_t s);
 // q, k: [B, H, S_pad, hd]; v^T: [B, H, hd, S_pad] (bf16 path) or v: [B, H, S_pad, hd] (fp32 path);
 // bias: [B, S_pad] additive key bias (KEY_KEEP for a kept key, -inf for an
 // excluded one); o: [M, d] in residual row order.
-// The bf16 kernel works in log2 units with a fixed softmax reference: it takes q
-// pre-multiplied by ATTN_BF16_Q_SCALE = log2(e)/sqrt(256) and the bias with
-// KEY_KEEP = ATTN_BF16_KEY_KEEP = -16.25 log2(e) (QK-norm bounds every logit
-// q.k/16 to [-16, 16]); the fp32 kernel takes plain q and KEY_KEEP = 0.
-constexpr float ATTN_BF16_Q_SCALE = 1.4426950408889634f / 16.0f;
-constexpr float ATTN_BF16_KEY_KEEP = -16.25f * 1.4426950408889634f;
+// The bf16 kernel uses a fixed softmax reference: it takes q pre-multiplied by
+// ATTN_BF16_Q_SCALE = 1/sqrt(256) (a power of two, so the bf16 q it reads is the
+// bf16-rounded normalised q, scaled exactly) and the bias with KEY_KEEP =
+// ATTN_BF16_KEY_KEEP = -24 ln 2, and forms p = 2^((s + bias) log2 e) = e^s 2^-24
+// for the logit s = q.k/16 (QK-norm bounds s to [-16, 16], so p < 1 and no
+// denormal). The shift is a whole power of two, so p's bf16 rounding is that
+// of e^s. The fp32 kernel takes plain q and KEY_KEEP = 0.
+constexpr float ATTN_BF16_Q_SCALE = 1.0f / 16.0f;
+constexpr float ATTN_BF16_KEY_KEEP = -24.0f * 0.69314718055994531f;
+constexpr float ATTN_LOG2E = 1.4426950408889634f;
 // part: scratch for split query tiles, room for part_pieces pieces of
 // attention_bf16_part_floats(1) floats each (NULL: no splitting; at most n_cu
 // pieces are used); n_cu: compute units of the device. o8 != NULL: the output
@@ -130,6 +148,30 @@ hipError_t umt5_rel_bias_rows(const float* rel_bias, int L, int H, int T, float*
 // out [B*T, d] bf16; T <= 512
 hipError_t umt5_attention(const bf16_t* qkv, int B, int T, int H, int d, const float* bias_rows,
                           const uint8_t* mask, bf16_t* out, hipStream_t s);
+
+// ------------------------------------------------------------------ VAE decode
+// Activations NHWC [B, P, C] (P pixels per sample).
+// out[b, p, :Cpad] = bf16(Wpq (lat[b, :, p] / scaling) + bpq), zero past Cl; Cl <= 32.
+hipError_t vae_prep(const float* lat, int B, int Cl, long P, float scaling, const float* wpq, const float* bpq,
+                    int Cpad, bf16_t* out, hipStream_t s);
+// GroupNorm statistics of x [B, P, C] over G groups: stats[b G + g] = (mean, 1/sqrt(var + eps));
+// part: scratch of gn_part_floats(B, P, G) floats. C a multiple of 4 G, C <= 1024.
+size_t gn_part_floats(int B, long P, int G);
+hipError_t group_norm_stats(const float* x, int B, long P, int C, int G, float eps, float4* part, float2* stats,
+                            hipStream_t s);
+// y = bf16(act((x - mean) rstd gamma + beta)), act = SiLU when silu != 0.
+hipError_t group_norm_apply(const float* x, int B, long P, int C, int G, const float2* stats, const float* gamma,
+                            const float* beta, int silu, bf16_t* y, hipStream_t s);
+// P[r, j] = softmax_j(scale S[r, j]) over j < n, 0 for n <= j < ld; rows x ld, bf16 out.
+hipError_t softmax_rows(const float* S, long rows, long ld, int n, float scale, bf16_t* P, hipStream_t s);
+// vt[c, p] = src[p lds + c] (p < P), zero for P <= p < Ppad; vt is [C][Ppad].
+hipError_t transpose_cols(const bf16_t* src, long lds, long P, int C, long Ppad, bf16_t* vt, hipStream_t s);
+// 3x3 convolution (zero padding) of a [B, H, W, Cin] bf16 to Cout <= 4 channels, image NCHW fp32;
+// w [Cout][9 Cin] bf16 in the GEMM's column order (tap Cin + c), bias fp32.
+hipError_t conv_out3x3(const bf16_t* a, int B, int H, int W, int Cin, const bf16_t* w, const float* bias, int Cout,
+                       float* img, hipStream_t s);
+enum VaePack { VAE_PACK_BF16 = 0, VAE_PACK_CONV3 = 1, VAE_PACK_F32R = 2 };
+hipError_t vae_pack(const float* src, long n, long first, void* dst, int mode, int cin, int cpad, hipStream_t s);
 
 // resid[m, n] += sum over s = 0 .. ks-1, in that order, of part[s][m][n] (the EPI_PARTIAL output)
 hipError_t splitk_resid(const float* part, int ks, long M, int N, float* resid, hipStream_t s);

@@ -10,21 +10,23 @@
 // output o [M, d] in residual-row order, bf16, or MXFP8 (E4M3 values plus one
 // power-of-two scale per 32 head-dim values) for the MXFP8 out-projection.
 //
-// Scaled inputs: q arrives multiplied by log2(e)/16 (the QKV epilogue applies
-// it before rounding to bf16) and the key bias holds -16.25 log2(e) for a kept
-// key and -inf for an excluded one, so p = exp2(k.q' + bias) needs no other
-// arithmetic. Softmax reference: QK-norm (LayerNorm over the head dim, no
-// affine) gives every normalised q and k a norm of at most sqrt(256) = 16, so
-// every logit q.k / 16 lies in [-16, 16]; the kernel subtracts the fixed
-// reference 16.25 (a margin for bf16 rounding) instead of a running maximum:
-// softmax is invariant to the shift, p stays in [e^-33, 1] (no overflow, no
-// denormals), and the running-max bookkeeping and the rescaling of O disappear.
-// With a fixed reference, partial sums over key tiles simply add.
+// Scaled inputs: q arrives multiplied by 1/16 (the QKV epilogue applies it
+// before rounding to bf16; a power of two, so it commutes with the rounding) and
+// the key bias holds -24 ln 2 for a kept key and -inf for an excluded one, so
+// p = exp2((k.q' + bias) log2 e). Softmax reference: QK-norm (LayerNorm over the
+// head dim, no affine) gives every normalised q and k a norm of at most
+// sqrt(256) = 16, so every logit q.k / 16 lies in [-16, 16]; the kernel
+// subtracts the fixed reference 24 ln 2 = 16.64 instead of a running maximum:
+// softmax is invariant to the shift, p = e^s 2^-24 stays in [2^-48, 1) (no
+// overflow, no denormals), the running-max bookkeeping and the rescaling of O
+// disappear, and since the shift is a whole power of two the bf16 rounding of p
+// for the P V product is that of e^s. With a fixed reference, partial sums over
+// key tiles simply add.
 //
 // One workgroup = 4 waves = 128 queries of one (b, h); each wave owns 32 queries
 // and keeps them in registers as MFMA B operands. Per 64-key tile:
 //   S^T = K Q'^T + bias  (A = K rows from LDS) -> one query per lane (lane & 31),
-//   P = exp2(S^T),
+//   P = exp2(S^T log2 e),
 //   O^T += V^T P^T (A = v^T from LDS, B = P straight from the S^T registers).
 // The K rows each lane feeds to the S^T MFMA are permuted (bits 2 and 3 of the
 // row index swapped) so that the accumulator registers a lane holds are, per
@@ -267,7 +269,7 @@ void k_attention_bf16(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K
         auto p_step = [&](int k) {
             const int e = k & 7, s4 = k >> 3;
             const int tt = s4 >> 1, i = 2 * (s4 & 1) + (e >> 2), j = e & 3;
-            pf[e] = __builtin_amdgcn_exp2f(cur[tt][i * 4 + j]);   // v_exp_f32; argument >= -48 or -inf
+            pf[e] = __builtin_amdgcn_exp2f(cur[tt][i * 4 + j] * ATTN_LOG2E);   // v_exp_f32; argument >= -48 or -inf
             psum += pf[e];
             if (e == 7) pb[s4] = pack8(pf);
         };

@@ -5,7 +5,7 @@
 // projections in token-major layout.
 //
 // Three launches on the caller's stream: the QK-norm pack (q and k normalised
-// over the head dimension, q pre-scaled for the attention kernel's log2-unit
+// over the head dimension, q pre-scaled by 1/16 for the attention kernel's
 // fixed-reference softmax, both scattered to [B, H, S_pad, 256]), the v^T pack
 // ([B, H, 256, S_pad] through an LDS transpose) plus the key bias, then the
 // attention kernel the transformer forward uses (and its split-tile combine).

@@ -181,6 +181,30 @@ def attention(q, k, v, key_valid, scale):
     return out
 
 
+def attention_bf16_operands(q, k, v, key_valid, scale):
+    """The attention of the MXFP8 model: softmax(q k^T * scale) v with the two
+    products taking bfloat16 operands -- q and k (after the QK-norm) and v are
+    rounded to bfloat16 (round_bf16), and so are the unnormalised probabilities
+    e = exp(logit) that multiply v; the normaliser is the sum of the unrounded e,
+    and the products accumulate in the working precision. Without the roundings
+    this is `attention` exactly (the max shift cancels in the ratio); no shift is
+    taken here because the QK-norm bounds every logit by sqrt(hd)^2 * scale
+    (16 at hd = 256), so e cannot overflow, and a shift by a whole power of two
+    would leave the rounding of e unchanged anyway.
+    """
+    B, Hh, S, hd = q.shape
+    dt = q.dtype
+    qb, kb_all, vb_all = round_bf16(q).astype(dt), round_bf16(k).astype(dt), round_bf16(v).astype(dt)
+    out = np.empty_like(q)
+    for b in range(B):
+        valid = np.asarray(key_valid[b]) != 0
+        kb, vb = kb_all[b][:, valid, :], vb_all[b][:, valid, :]
+        for h in range(Hh):
+            e = np.exp((qb[b, h] @ kb[h].T) * scale)
+            out[b, h] = (round_bf16(e).astype(dt) @ vb[h]) / e.sum(axis=1, keepdims=True)
+    return out
+
+
 def feed_forward(n, w1, w2, w3, mx=False):
     """SiLU-gated FFN: (silu(n W1^T) * (n W2^T)) W3^T ([PIPE] 深入源码 (前馈网络)).
     mx: the hidden activations are MXFP8-quantized before W3 (operands n and the
@@ -198,8 +222,9 @@ def _mod6(temb, ada):
 # FFN products take MXFP8 operands -- the LayerNorm + modulate outputs, the
 # attention output, the SiLU-gated hidden activations and the weights of those
 # four products are quantized along their contraction axis (mxfp8_qdq) and the
-# products accumulate in the working precision. Attention itself and everything
-# else are unchanged.
+# products accumulate in the working precision. Attention takes bfloat16
+# operands (attention_bf16_operands): the E4M3 codes of its output are decided
+# from the values that bf16 attention produces. Everything else is unchanged.
 MX_WEIGHTS = ("wq", "wk", "wv", "wo", "ff1", "ff2", "ff3")
 
 
@@ -239,8 +264,9 @@ def joint_block(cfg, blk_img, blk_txt, temb, x_txt, x_img, key_valid, dtype=np.f
     n_txt = _mxq(modulate(layer_norm(x_txt, eps), mt[0], mt[1]), mx)
     qi, ki, vi = _qkv(n_img, blk_img, cfg, dtype)
     qt, kt, vt = _qkv(n_txt, blk_txt, cfg, dtype)
-    o = attention(np.concatenate([qt, qi], axis=2), np.concatenate([kt, ki], axis=2),
-                  np.concatenate([vt, vi], axis=2), key_valid, scale)
+    attn = attention_bf16_operands if mx else attention
+    o = attn(np.concatenate([qt, qi], axis=2), np.concatenate([kt, ki], axis=2),
+             np.concatenate([vt, vi], axis=2), key_valid, scale)
     o = _mxq(_merge(o), mx)
     o_txt, o_img = o[:, :Nt], o[:, Nt:]
     x_img = x_img + mi[2][:, None, :] * (o_img @ blk_img["wo"].T)
@@ -265,7 +291,8 @@ def single_block(cfg, blk, temb, x, key_valid, dtype=np.float32, mx=False):
     m = _mod6(temb, blk["ada"])
     n = _mxq(modulate(layer_norm(x, eps), m[0], m[1]), mx)
     q, k, v = _qkv(n, blk, cfg, dtype)
-    o = _mxq(_merge(attention(q, k, v, key_valid, scale)), mx)
+    attn = attention_bf16_operands if mx else attention
+    o = _mxq(_merge(attn(q, k, v, key_valid, scale)), mx)
     x = x + m[2][:, None, :] * (o @ blk["wo"].T)
     n = _mxq(modulate(layer_norm(x, eps), m[3], m[4]), mx)
     return x + m[5][:, None, :] * feed_forward(n, blk["ff1"], blk["ff2"], blk["ff3"], mx)

@@ -142,13 +142,87 @@ def test_mx_forward_uses_quantized_operands_only_where_stated():
     np.testing.assert_array_equal(oracle.mxfp8_qdq(qb["ff3"]), qb["ff3"])
 
 
+def _torch_bf16(a):
+    """bfloat16 rounding by torch's own cast (an implementation independent of
+    oracle.round_bf16), returned as float32."""
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(torch.bfloat16).float().numpy()
+
+
+def _attention_bf16_by_hand(q, k, v, kv, scale):
+    """softmax(q k^T scale) v with q, k, v and exp(logit) rounded by torch's bf16
+    cast, normalised by the sum of the unrounded exponentials; keys with kv == 0
+    left out."""
+    out = np.empty_like(q)
+    qb, kb, vb = _torch_bf16(q), _torch_bf16(k), _torch_bf16(v)
+    for b in range(q.shape[0]):
+        keep = kv[b] != 0
+        for h in range(q.shape[1]):
+            e = np.exp((qb[b, h] @ kb[b, h][keep].T) * scale)
+            out[b, h] = (_torch_bf16(e) @ vb[b, h][keep]) / e.sum(axis=1, keepdims=True)
+    return out
+
+
+def test_bf16_operand_attention_hand_case():
+    """One query, two kept keys and one excluded key, head dim 16, scale 1/4:
+    q = 1 + 2^-10 rounds to 1 in bf16, so the logits are exactly 0 and 1; e^1 =
+    2.71828 (float32) rounds to 2.71875 in bf16; v0 = 0.1 rounds to
+    0.10009765625. The output is (1 * 0.10009765625 + 2.71875 * 3) / (1 + e^1):
+    rounded probabilities in the numerator, unrounded ones in the normaliser."""
+    hd = 16
+    q = np.zeros((1, 1, 1, hd), np.float32)
+    q[0, 0, 0, 0] = 1 + 2.0 ** -10
+    k = np.zeros((1, 1, 3, hd), np.float32)
+    k[0, 0, 1, 0] = 4.0
+    k[0, 0, 2, 0] = 8.0                      # excluded below
+    v = np.zeros((1, 1, 3, hd), np.float32)
+    v[0, 0, :, 3] = [0.1, 3.0, 1000.0]
+    kv = np.array([[1, 1, 0]], np.uint8)
+    got = oracle.attention_bf16_operands(q, k, v, kv, np.float32(0.25))
+    e1 = float(np.exp(np.float32(1.0)))
+    want = (0.10009765625 + 2.71875 * 3.0) / (1.0 + e1)
+    assert abs(e1 - math.e) < 4e-7          # float32 exp, within an ulp either way
+    assert abs(float(got[0, 0, 0, 3]) - want) <= 2e-7 * want
+    assert np.all(got[0, 0, 0, [0, 1, 2, 4, 15]] == 0)
+    # the plain softmax differs visibly: the roundings are really there
+    plain = oracle.attention(q, k, v, kv, np.float32(0.25))
+    assert abs(float(plain[0, 0, 0, 3]) - want) > 1e-4
+
+
+def test_bf16_operand_attention_against_torch_casts_and_plain_softmax():
+    """Random ragged case: equal to the composition with torch's bf16 cast; within
+    bf16's relative half-ulp bound (2^-9 per rounded operand) of the float64 plain
+    attention; with q = 0 the output is the mean of the bf16-rounded values of
+    the kept keys, exactly."""
+    rng = np.random.default_rng(21)
+    B, H, S, hd = 2, 3, 37, 16
+    q, k, v = (rng.standard_normal((B, H, S, hd)).astype(np.float32) for _ in range(3))
+    q, k = T.layer_norm(q, np.float32(1e-6)), T.layer_norm(k, np.float32(1e-6))
+    kv = np.ones((B, S), np.uint8)
+    kv[1, 20:30] = 0
+    sc = np.float32(0.25)
+    got = oracle.attention_bf16_operands(q, k, v, kv, sc)
+    np.testing.assert_allclose(got, _attention_bf16_by_hand(q, k, v, kv, sc), rtol=0, atol=1e-6)
+    exact = oracle.attention(q.astype(np.float64), k.astype(np.float64), v.astype(np.float64), kv, 0.25)
+    err = np.abs(got - exact).max() / np.abs(v).max()
+    # q, k roundings move a logit by <= 2 * 2^-9 * |q||k| * scale = 2^-8 * 4; e and v by 2^-9 each
+    assert 1e-5 < err < 4 * 2.0 ** -8 + 2 * 2.0 ** -9, err
+    z = oracle.attention_bf16_operands(np.zeros_like(q), k, v, kv, sc)
+    vb = oracle.round_bf16(v).astype(np.float64)
+    for b in range(B):
+        keep = kv[b] != 0
+        want = vb[b][:, keep].mean(axis=1)
+        np.testing.assert_allclose(z[b, :, 0], want, rtol=1e-6, atol=1e-7)
+
+
 def _single_block_by_hand(cfg, blk, temb, x, kv, quant_points):
     """A single DiT block with MXFP8 quantize-dequantize applied exactly at the
     named activation points (a subset of 'ln1', 'attn', 'ln2', 'ffh') and to the
-    weights of the QKV, out-projection and FFN products; everything else in
-    float32. Composed from the block's equations: adaLN-Zero with six vectors,
-    LN + modulate, bias-free q/k/v with per-head LayerNorm, softmax attention,
-    gated out-projection, LN + modulate, SiLU-gated FFN, gated residual."""
+    weights of the QKV, out-projection and FFN products, and ('bf16attn' in the
+    subset) attention on bf16 operands; everything else in float32. Composed from
+    the block's equations: adaLN-Zero with six vectors, LN + modulate, bias-free
+    q/k/v with per-head LayerNorm, softmax attention, gated out-projection,
+    LN + modulate, SiLU-gated FFN, gated residual."""
     f32 = np.float32
     qd = lambda a, point: oracle.mxfp8_qdq(a) if point in quant_points else a
     Wq = {k: oracle.mxfp8_qdq(blk[k]) for k in ("wq", "wk", "wv", "wo", "ff1", "ff2", "ff3")}
@@ -163,7 +237,8 @@ def _single_block_by_hand(cfg, blk, temb, x, kv, quant_points):
     q = T.layer_norm(heads(n1 @ Wq["wq"].T), eps)
     k = T.layer_norm(heads(n1 @ Wq["wk"].T), eps)
     v = heads(n1 @ Wq["wv"].T)
-    o = T.attention(q, k, v, kv, f32(1.0 / np.sqrt(hd)))
+    attn = _attention_bf16_by_hand if "bf16attn" in quant_points else T.attention
+    o = attn(q, k, v, kv, f32(1.0 / np.sqrt(hd)))
     o = qd(o.transpose(0, 2, 1, 3).reshape(B, S, d), "attn")
     x1 = x + g1[:, None, :] * (o @ Wq["wo"].T)
     n2 = qd(T.layer_norm(x1, eps) * (1 + sc2[:, None, :]) + sh2[:, None, :], "ln2")
@@ -174,8 +249,8 @@ def _single_block_by_hand(cfg, blk, temb, x, kv, quant_points):
 def test_mx_single_block_quantizes_exactly_the_four_activation_points():
     """single_block(mx=True) equals the block composed by hand with MXFP8 applied at
     the LN + modulate outputs (both), the attention output and the FFN hidden
-    activations, and at no other activation; dropping any one of the four points
-    changes the result, so each of them is pinned."""
+    activations, and at no other activation, with attention on bf16 operands;
+    dropping any one of the five changes the result, so each of them is pinned."""
     cfg = oracle.TINY
     W = oracle.Weights.seeded(cfg, seed=0)
     rng = np.random.default_rng(11)
@@ -189,7 +264,7 @@ def test_mx_single_block_quantizes_exactly_the_four_activation_points():
     # adaLN rows scaled up so the gates and modulations are O(1) and every branch
     # moves the residual visibly
     blk["ada"] = blk["ada"] * np.float32(20.0)
-    points = ("ln1", "attn", "ln2", "ffh")
+    points = ("ln1", "attn", "ln2", "ffh", "bf16attn")
     got = T.single_block(cfg, blk, temb, x, kv, np.float32, mx=True)
     want = _single_block_by_hand(cfg, blk, temb, x, kv, points)
     np.testing.assert_allclose(got, want, rtol=0, atol=1e-5 * np.abs(want).max())
@@ -215,6 +290,6 @@ def test_mx_joint_block_quantizes_the_same_points_per_stream():
     blk = {k: W["single0." + k] for k in ("ada", "wq", "wk", "wv", "wo", "ff1", "ff2", "ff3")}
     blk["ada"] = blk["ada"] * np.float32(20.0)
     xt, xi = T.joint_block(cfg, blk, blk, temb, x[:, :Nt], x[:, Nt:], kv, np.float32, mx=True)
-    want = _single_block_by_hand(cfg, blk, temb, x, kv, ("ln1", "attn", "ln2", "ffh"))
+    want = _single_block_by_hand(cfg, blk, temb, x, kv, ("ln1", "attn", "ln2", "ffh", "bf16attn"))
     got = np.concatenate([xt, xi], 1)
     np.testing.assert_allclose(got, want, rtol=0, atol=1e-5 * np.abs(want).max())
