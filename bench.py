@@ -249,6 +249,65 @@ def text_encoder_leg(args, af, torch, steps, warmup):
             "tflops": flops / (ms * 1e-3) / 1e12, "pct_peak_bf16": 100.0 * flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
 
 
+def vae_flops(cfg, B, h, w):
+    """Algorithmic FLOPs of one decode (2 per multiply-add; convolutions over their
+    real input channels, attention's two products and four projections)."""
+    ch = list(cfg.block_out_channels)[::-1]
+    P = h * w
+    conv = lambda P_, cin, cout, k: 2.0 * B * P_ * k * cin * cout
+
+    def res(P_, cin, cout):
+        return conv(P_, cin, cout, 9) + conv(P_, cout, cout, 9) + (conv(P_, cin, cout, 1) if cin != cout else 0.0)
+
+    f = conv(P, cfg.latent_channels, cfg.latent_channels, 1) + conv(P, cfg.latent_channels, ch[0], 9)
+    C = ch[0]
+    f += 2 * res(P, C, C) + 4 * conv(P, C, C, 1) + 4.0 * B * P * P * C
+    cin = C
+    for l in range(4):
+        for r in range(cfg.layers_per_block + 1):
+            f += res(P, cin, ch[l])
+            cin = ch[l]
+        if l < 3:
+            P *= 4
+            f += conv(P, cin, cin, 9)
+    return f + conv(P, cin, cfg.out_channels, 9)
+
+
+def vae_leg(args, af, torch, steps, warmup):
+    """The VAE decode (AutoencoderKL decoder, widths 512/512/256/128, three ResNet blocks
+    per level, mid-block attention over the 128 x 128 latent pixels) of 4 latents
+    [4, 4, 128, 128] into 4 images of 1024 x 1024, random bf16 weights. Returns the
+    timing object."""
+    import seeded_inputs
+    B, h, w = 4, 128, 128
+    cfg = af.vae_make_config(max_batch=B, max_latent_h=h, max_latent_w=w)
+    dec = af.VAEDecoder(cfg, 0)
+    dec.load_seeded_weights(threads=_cpu_threads())
+    lat = torch.from_numpy(seeded_inputs.latents(B, cfg.latent_channels, h, w, first_index=300)).cuda()
+    out = torch.empty((B, cfg.out_channels, 8 * h, 8 * w), dtype=torch.float32, device="cuda")
+    for _ in range(warmup):
+        dec.decode(lat, out=out)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out).all()), "non-finite VAE output"
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        dec.decode(lat, out=out)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    flops = vae_flops(cfg, B, h, w)
+    dec.close()
+    return {"workload": f"VAE decode (AutoencoderKL decoder, widths {list(cfg.block_out_channels)[::-1]}, "
+                        f"{cfg.layers_per_block + 1} ResNet blocks per level, mid-block attention over {h * w} "
+                        f"pixels) of {B} latents [{B}, {cfg.latent_channels}, {h}, {w}] into {B} images of "
+                        f"{8 * h}x{8 * w}; seeded random bf16 weights",
+            "ms_per_decode": ms, "value": B * 1000.0 / ms, "unit": "images/s", "flops_per_decode": flops,
+            "tflops": flops / (ms * 1e-3) / 1e12, "pct_peak_bf16": 100.0 * flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+
+
 def sampling_loop_bench(args, af, torch):
     """--sampling-loop: the 25-step CFG loop for 4 images at 1024^2 (transformer batch 8)
     as its own JSON line; --steps counts loops."""
@@ -389,6 +448,10 @@ def main():
                     help="time only the text encoder (8 prompts x 256 tokens) and print its own line")
     ap.add_argument("--no-text-encoder-leg", action="store_true",
                     help="skip the text-encoder timing reported beside the transformer line")
+    ap.add_argument("--vae", action="store_true",
+                    help="time only the VAE decode (4 latents of 128 x 128 into 1024 x 1024 images) and print its own line")
+    ap.add_argument("--no-vae-leg", action="store_true",
+                    help="skip the VAE-decode timing reported beside the transformer line")
     ap.add_argument("--no-graph-leg", action="store_true",
                     help="skip the graph-replay timing reported beside the eager line")
     ap.add_argument("--no-extra-legs", action="store_true",
@@ -425,6 +488,16 @@ def main():
                           "ms_per_step": leg["ms_per_encode"], "higher_is_better": True, "scaling": "weak",
                           "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
                           "config": {"workload": leg["workload"], "global_batch": 8, "seq_len": 256,
+                                     "parallelism": "single GPU"},
+                          "tflops": leg["tflops"], "pct_peak_bf16": leg["pct_peak_bf16"]}))
+        return
+    if args.vae:
+        leg = vae_leg(args, af, torch, args.steps, args.warmup)
+        print(json.dumps({"metric": "VAE decode images/s (4 latents 128x128 -> 1024x1024)", "value": leg["value"],
+                          "unit": "images/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                          "ms_per_step": leg["ms_per_decode"], "higher_is_better": True, "scaling": "weak",
+                          "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+                          "config": {"workload": leg["workload"], "global_batch": 4, "seq_len": 16384,
                                      "parallelism": "single GPU"},
                           "tflops": leg["tflops"], "pct_peak_bf16": leg["pct_peak_bf16"]}))
         return
@@ -606,6 +679,15 @@ def main():
         te = text_encoder_leg(args, af, torch, args.steps, args.warmup)
         print(f"[bench] text encoder: {te['ms_per_encode']:.2f} ms/encode", file=sys.stderr, flush=True)
 
+    vae = None
+    if not args.no_vae_leg and not args.mxfp8:
+        if te is None:
+            model.close()
+            del model
+            torch.cuda.synchronize()
+        vae = vae_leg(args, af, torch, args.steps, args.warmup)
+        print(f"[bench] VAE decode: {vae['ms_per_decode']:.2f} ms per 4 images", file=sys.stderr, flush=True)
+
     cpu = None
     if not args.no_cpu_baseline:
         print(f"[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
@@ -640,6 +722,7 @@ def main():
         "sampling_loop": loop,
         "mxfp8_model": mx_leg,
         "text_encoder": te,
+        "vae_decode": vae,
         "cpu_baseline": cpu,
         "kernels": kernels,
         "setup_s": setup_s,

@@ -47,6 +47,14 @@ class AfUmt5Config(C.Structure):
     ]
 
 
+class AfVaeConfig(C.Structure):
+    _fields_ = [
+        ("latent_channels", C.c_int), ("out_channels", C.c_int), ("block_out_channels", C.c_int * 4),
+        ("layers_per_block", C.c_int), ("norm_groups", C.c_int), ("norm_eps", C.c_float),
+        ("scaling_factor", C.c_float), ("max_batch", C.c_int), ("max_latent_h", C.c_int), ("max_latent_w", C.c_int),
+    ]
+
+
 def _load():
     if not os.path.exists(_LIB_PATH):
         raise ImportError(f"{_LIB_PATH} is missing: build it with python -m flow_matching_mmdit_amd.build")
@@ -54,6 +62,7 @@ def _load():
     P, I, SZ, F, D, V = C.c_void_p, C.c_int, C.c_size_t, C.c_float, C.c_double, None
     cfgp = C.POINTER(AfConfig)
     ucfgp = C.POINTER(AfUmt5Config)
+    vcfgp = C.POINTER(AfVaeConfig)
     sig = {
         "af_config_default": (I, [cfgp]),
         "af_check_shapes": (I, [cfgp, I, I, I, I]),
@@ -83,6 +92,15 @@ def _load():
         "af_umt5_encode": (I, [P, P, P, I, I, P, P]),
         "af_umt5_encode_taps": (I, [P, P, P, I, I, I, P, P]),
         "af_umt5_destroy": (V, [P]),
+        "af_vae_config_default": (I, [vcfgp]),
+        "af_vae_weight_count": (I, [vcfgp, C.POINTER(I), C.POINTER(SZ)]),
+        "af_vae_weight_info": (I, [vcfgp, I, C.c_char_p, I, C.POINTER(C.c_int64), C.POINTER(C.c_int64),
+                                   C.POINTER(SZ)]),
+        "af_vae_create": (I, [vcfgp, I, C.POINTER(P)]),
+        "af_vae_load_weights": (I, [P, P, SZ, SZ, P]),
+        "af_vae_decode": (I, [P, P, I, I, I, P, P]),
+        "af_vae_decode_taps": (I, [P, P, I, I, I, I, P, P]),
+        "af_vae_destroy": (V, [P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -99,7 +117,9 @@ EXPORTED = (
     "af_attention_noalloc", "af_attention_noalloc_max_bytes",
     "af_sigma_schedule", "af_destroy", "af_status_string",
     "af_last_error", "af_umt5_config_default", "af_umt5_weight_count", "af_umt5_weight_info",
-    "af_umt5_create", "af_umt5_load_weights", "af_umt5_encode", "af_umt5_encode_taps", "af_umt5_destroy")
+    "af_umt5_create", "af_umt5_load_weights", "af_umt5_encode", "af_umt5_encode_taps", "af_umt5_destroy",
+    "af_vae_config_default", "af_vae_weight_count", "af_vae_weight_info", "af_vae_create", "af_vae_load_weights",
+    "af_vae_decode", "af_vae_decode_taps", "af_vae_destroy")
 
 
 class AfError(RuntimeError):
@@ -578,4 +598,134 @@ class UMT5Encoder:
         self._check_out(out, B, T)
         _check(_lib.af_umt5_encode_taps(self._h, C.c_void_p(ids.data_ptr()), mptr, B, T, stop_after_layer,
                                         C.c_void_p(out.data_ptr()), _stream_ptr(stream)))
+        return out
+
+
+# ----------------------------------------------------------------------------- VAE decode
+
+def vae_make_config(**kw) -> AfVaeConfig:
+    """The AutoencoderKL decoder defaults with any field overridden by keyword
+    (block_out_channels as a 4-sequence)."""
+    c = AfVaeConfig()
+    _check(_lib.af_vae_config_default(C.byref(c)))
+    for k, v in kw.items():
+        if not hasattr(c, k):
+            raise KeyError(k)
+        if k == "block_out_channels":
+            v = (C.c_int * 4)(*v)
+        setattr(c, k, v)
+    return c
+
+
+def af_vae_weight_count(cfg: AfVaeConfig):
+    n, tot = C.c_int(), C.c_size_t()
+    _check(_lib.af_vae_weight_count(C.byref(cfg), C.byref(n), C.byref(tot)))
+    return n.value, tot.value
+
+
+def af_vae_weight_info(cfg: AfVaeConfig, index: int):
+    name = C.create_string_buffer(128)
+    r, c, o = C.c_int64(), C.c_int64(), C.c_size_t()
+    _check(_lib.af_vae_weight_info(C.byref(cfg), index, name, 128, C.byref(r), C.byref(c), C.byref(o)))
+    return name.value.decode(), r.value, c.value, o.value
+
+
+def vae_weight_recipe(name: str):
+    """Synthetic init (std, mean) by the tensor's suffix: kernels, matrices (.w) and
+    biases (.b) N(0, 0.02^2); GroupNorm scales (.g) N(1, 0.1^2); GroupNorm shifts
+    (.n) N(0, 0.02^2)."""
+    return {"w": (0.02, 0.0), "b": (0.02, 0.0), "g": (0.1, 1.0), "n": (0.02, 0.0)}[name.rsplit(".", 1)[1]]
+
+
+class VAEDecoder:
+    """One VAE-decoder handle on one device; latents in, images out."""
+
+    def __init__(self, cfg: AfVaeConfig, device: int = 0):
+        self.cfg = cfg
+        self.device = device
+        h = C.c_void_p()
+        _check(_lib.af_vae_create(C.byref(cfg), device, C.byref(h)))
+        self._h = h
+        n, total = af_vae_weight_count(cfg)
+        self.weights = [af_vae_weight_info(cfg, i) for i in range(n)]
+        self.total_floats = total
+
+    def close(self):
+        if getattr(self, "_h", None):
+            _lib.af_vae_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def load_weights(self, host: np.ndarray, offset: int = 0, stream=None):
+        a = np.ascontiguousarray(host, dtype=np.float32).ravel()
+        _check(_lib.af_vae_load_weights(self._h, C.c_void_p(a.ctypes.data), offset, a.size, _stream_ptr(stream)))
+
+    def load_seeded_weights(self, seed: int | None = None, threads: int = 8):
+        """Draws every canonical tensor from seeded_inputs (stream (seed, index)) and loads it."""
+        import seeded_inputs
+        seed = seeded_inputs.SEED_VAE_WEIGHTS if seed is None else seed
+
+        def draw(i):
+            name, rows, cols, off = self.weights[i]
+            std, mean = vae_weight_recipe(name)
+            return off, seeded_inputs.normal(seed, i, (rows * cols,), std, mean)
+
+        n = len(self.weights)
+        win = 2 * max(1, threads)
+        with ThreadPoolExecutor(max(1, threads)) as ex:
+            for w0 in range(0, n, win):
+                for off, a in ex.map(draw, range(w0, min(n, w0 + win))):
+                    self.load_weights(a, off)
+
+    def _args(self, latents, out, out_shape):
+        import torch
+        _need(latents.dtype == torch.float32 and latents.is_contiguous() and latents.dim() == 4
+              and latents.shape[1] == self.cfg.latent_channels,
+              "latents must be contiguous float32 [B, latent_channels, h, w]")
+        if out is not None:
+            _need(out.dtype == torch.float32 and out.is_contiguous() and tuple(out.shape) == tuple(out_shape),
+                  f"out must be contiguous float32 {list(out_shape)}")
+        _on_device(latents, "latents", self.device)
+        if out is not None:
+            _on_device(out, "out", self.device)
+        B, _, h, w = latents.shape
+        return B, h, w
+
+    def decode(self, latents, out=None, stream=None):
+        """latents [B, latent_channels, h, w] -> image [B, out_channels, 8h, 8w] (fp32)."""
+        import torch
+        B, _, h, w = latents.shape if latents.dim() == 4 else (0, 0, 0, 0)
+        shape = (B, self.cfg.out_channels, 8 * h, 8 * w)
+        B, h, w = self._args(latents, out, shape)
+        if out is None:
+            out = torch.empty(shape, dtype=torch.float32, device=latents.device)
+        _check(_lib.af_vae_decode(self._h, C.c_void_p(latents.data_ptr()), B, h, w, C.c_void_p(out.data_ptr()),
+                                  _stream_ptr(stream)))
+        return out
+
+    def tap_shape(self, B: int, h: int, w: int, stop_after: int):
+        """NHWC shape of the activation af_vae_decode_taps writes after stage stop_after."""
+        ch = list(self.cfg.block_out_channels)[::-1]
+        if stop_after <= 1:
+            return (B, h, w, ch[0])
+        lvl = stop_after - 2
+        f = 2 ** min(lvl + 1, 3)
+        return (B, f * h, f * w, ch[lvl])
+
+    def decode_taps(self, latents, stop_after: int, out=None, stream=None):
+        """The fp32 NHWC activation after stage stop_after (0 conv_in, 1 mid, 2 + l up level l)."""
+        import torch
+        _need(0 <= stop_after <= 5, "stop_after must be in 0 .. 5")
+        B, _, h, w = latents.shape if latents.dim() == 4 else (0, 0, 0, 0)
+        shape = self.tap_shape(B, h, w, stop_after)
+        B, h, w = self._args(latents, out, shape)
+        if out is None:
+            out = torch.empty(shape, dtype=torch.float32, device=latents.device)
+        _check(_lib.af_vae_decode_taps(self._h, C.c_void_p(latents.data_ptr()), B, h, w, stop_after,
+                                       C.c_void_p(out.data_ptr()), _stream_ptr(stream)))
         return out

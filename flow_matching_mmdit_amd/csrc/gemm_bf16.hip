@@ -152,7 +152,60 @@ void k_gemm_bf16(GemmLaunch L) {
     const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc((void*)Atile, (short)0, 0x7fffffff, 0x00020000);
     const __amdgpu_buffer_rsrc_t rW = __builtin_amdgcn_make_buffer_rsrc((void*)Wtile, (short)0, 0x7fffffff, 0x00020000);
     const int ldab = (int)lda * 2, ldwb = (int)ldw * 2;
-    auto issueA = [&](int t, int st) { issue_tile<NW, BM_>(rA, aoff, min(t, KT - 1) * BK * 2, ldab, slot_ptr(st), wave); };
+    // Implicit-GEMM 3x3 convolution (EPI_CONV with L.conv != 0): row m of the tile
+    // is output pixel (b, y, x), column k = tap Cin + c with tap = 3 (dy + 1) +
+    // (dx + 1) reads input pixel (b, y + dy, x + dx) (L.conv == 2: pixel
+    // ((y + dy) >> 1, (x + dx) >> 1) of the half-size input, the 2x nearest
+    // upsampling). A sub-tile's 32 columns lie in one tap (Cin is a multiple of
+    // 32), so each lane gathers its two rows' 16 bytes with per-lane offsets;
+    // pixels outside the image and rows past M get an offset past the buffer's
+    // end, which the buffer range check reads as zeros (the zero padding).
+    int cyy[PER], cxx[PER], cbb[PER];
+    uint32_t clc[PER];
+    bool conv_on = false;
+    __amdgpu_buffer_rsrc_t rAc = rA;
+    if constexpr (EPI == EPI_CONV) {
+        conv_on = L.conv != 0;
+        if (conv_on) {
+            const int Ho = L.conv == 2 ? 2 * L.cH : L.cH, Wo = L.conv == 2 ? 2 * L.cW : L.cW;
+#pragma unroll
+            for (int j = 0; j < PER; ++j) {
+                const int r = (wave * PER + j) * RPI + lane / CH;
+                const int m = m0 + r;
+                const int pb = m / (Ho * Wo), rem = m - pb * (Ho * Wo);
+                cbb[j] = pb;
+                cyy[j] = m < M ? rem / Wo : -(1 << 20);     // rows past M: never inside the image
+                cxx[j] = rem % Wo;
+                clc[j] = (uint32_t)(((lane % CH) ^ swz(r)) * 16);
+            }
+            rAc = __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, (int)L.a_bytes, 0x00020000);
+        }
+    }
+    auto issueA_conv = [&](int t, int st) {
+        const int k0 = min(t, KT - 1) * BK;
+        const int tap = k0 / L.cCin, c0 = k0 - tap * L.cCin;
+        const int dy = tap / 3 - 1, dx = tap - 3 * (tap / 3) - 1;
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int sy = cyy[j] + dy, sx = cxx[j] + dx;
+            uint32_t voff;
+            if (L.conv == 2) {
+                const bool in = (unsigned)sy < (unsigned)(2 * L.cH) && (unsigned)sx < (unsigned)(2 * L.cW);
+                const uint32_t pix = (uint32_t)((cbb[j] * L.cH + (sy >> 1)) * L.cW + (sx >> 1));
+                voff = in ? pix * (uint32_t)L.cCin * 2u + clc[j] : 0x80000000u;
+            } else {
+                const bool in = (unsigned)sy < (unsigned)L.cH && (unsigned)sx < (unsigned)L.cW;
+                const uint32_t pix = (uint32_t)((cbb[j] * L.cH + sy) * L.cW + sx);
+                voff = in ? pix * (uint32_t)L.cCin * 2u + clc[j] : 0x80000000u;
+            }
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rAc, (lds_void*)(slot_ptr(st) + (wave * PER + j) * 512), 16, voff,
+                                                     c0 * 2, 0, 0);
+        }
+    };
+    auto issueA = [&](int t, int st) {
+        if (conv_on) issueA_conv(t, st);
+        else issue_tile<NW, BM_>(rA, aoff, min(t, KT - 1) * BK * 2, ldab, slot_ptr(st), wave);
+    };
     auto issueW = [&](int t, int st) {
         issue_tile<NW, BN_>(rW, woff, min(t, KT - 1) * BK * 2, ldwb, slot_ptr(st) + TILE, wave);
     };
@@ -214,15 +267,19 @@ hipError_t gemm_bf16(const GemmLaunch& L, hipStream_t s) {
     }
     if (LL.ngroups == 2 && LL.g[1].M == 0) LL.ngroups = 1;
     int total = 0;
-    for (int i = 0; i < LL.ngroups; ++i) total += tiles_m(LL.g[i].M) * (L.N / BN);
+    for (int i = 0; i < LL.ngroups; ++i) total += tiles_m(LL.g[i].M) * ((L.N + BN - 1) / BN);
     if (total == 0) return hipSuccess;
+    if (L.epi == EPI_CONV && (LL.ngroups != 1 || L.N % 128 != 0 || L.K % BK != 0 ||
+                              (L.conv && (L.cCin % BK != 0 || L.K != 9 * L.cCin || L.a_bytes >= (1L << 31)))))
+        return hipErrorInvalidValue;
     if (L.epi == EPI_PARTIAL && (LL.ngroups != 1 || L.ksplit < 1 || L.K % (BK * L.ksplit) != 0))
         return hipErrorInvalidValue;
     const int ks = L.epi == EPI_PARTIAL ? L.ksplit : 1;
     // 128 x 128 tiles (two workgroups per CU) when the 256 x 256 tiles, K ranges
     // included, would occupy at most half of the compute units: one round of the
     // small tiles then takes about half the time of the large tiles' round
-    const bool small = L.n_cu > 0 && 2 * total * ks <= L.n_cu && L.epi != EPI_QKV && L.epi != EPI_STORE_MAPPED;
+    const bool small = (L.n_cu > 0 && 2 * total * ks <= L.n_cu && L.epi != EPI_QKV && L.epi != EPI_STORE_MAPPED) ||
+                       (L.epi == EPI_CONV && L.N % BN != 0);
     if (small) {
         int t128 = 0;
         for (int i = 0; i < LL.ngroups; ++i) t128 += tiles_m<128>(LL.g[i].M) * (L.N / 128);
@@ -234,6 +291,7 @@ hipError_t gemm_bf16(const GemmLaunch& L, hipStream_t s) {
             case EPI_SWIGLU: AF_G128(EPI_SWIGLU); break;
             case EPI_GEGLU: AF_G128(EPI_GEGLU); break;
             case EPI_PARTIAL: AF_G128(EPI_PARTIAL); break;
+            case EPI_CONV: AF_G128(EPI_CONV); break;
             default: return hipErrorInvalidValue;
         }
 #undef AF_G128
@@ -253,6 +311,7 @@ hipError_t gemm_bf16(const GemmLaunch& L, hipStream_t s) {
         case EPI_SWIGLU: hipLaunchKernelGGL((k_gemm_bf16<EPI_SWIGLU, GEMM_WM, GEMM_WN>), grid, block, 0, s, LL); break;
         case EPI_GEGLU: hipLaunchKernelGGL((k_gemm_bf16<EPI_GEGLU, GEMM_WM, GEMM_WN>), grid, block, 0, s, LL); break;
         case EPI_PARTIAL: hipLaunchKernelGGL((k_gemm_bf16<EPI_PARTIAL, GEMM_WM, GEMM_WN>), grid, block, 0, s, LL); break;
+        case EPI_CONV: hipLaunchKernelGGL((k_gemm_bf16<EPI_CONV, GEMM_WM, GEMM_WN>), grid, block, 0, s, LL); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -123,7 +123,7 @@ __device__ __forceinline__ void epilogue(const GemmLaunch& L, f32x16 (&acc)[BM_ 
     if constexpr (EPI == EPI_PARTIAL) {
         // fp32 partial sums, split slab selected through row0 = split * M
         float* C = (float*)L.C;
-#pragma unroll 1
+#pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -132,9 +132,65 @@ __device__ __forceinline__ void epilogue(const GemmLaunch& L, f32x16 (&acc)[BM_ 
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt) C[(long)(row0 + m) * L.N + n0 + lc_base + nt * 32] = acc[mt][nt][r];
             }
+    } else if constexpr (EPI == EPI_CONV) {
+        // C[m, n] = acc + bias[n] (+ resid[m, n]); half a wave writes 32
+        // consecutive columns of one row. resid may be C itself (in place): every
+        // element is read and then written by the same lane. The residual loads of
+        // an mt block are all issued before its stores (rows past M read row M - 1
+        // and discard it, so the loads carry no branch), which keeps 16 NT loads
+        // in flight instead of one.
+        const float* cb = L.cbias;
+        const float* res = L.resid;
+        const int ncol = n0 + lc_base;
+        float bv[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) bv[nt] = cb ? cb[ncol + nt * 32] : 0.f;
+        auto row_of = [&](int mt, int r) { return m0 + lr_base + mt * 32 + (r >> 2) * 8 + (r & 3); };
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            float v[16][NT];
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) v[r][nt] = acc[mt][nt][r] + bv[nt];
+            if (res) {
+                float rv[16][NT];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const long ro = (long)(row0 + min(row_of(mt, r), M - 1)) * L.ldc + ncol;
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) rv[r][nt] = res[ro + nt * 32];
+                }
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) v[r][nt] += rv[r][nt];
+            }
+            if (L.c_bf16) {
+                bf16_t* C = (bf16_t*)L.C;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int m = row_of(mt, r);
+                    if (m >= M) continue;
+                    const long ro = (long)(row0 + m) * L.ldc + ncol;
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) C[ro + nt * 32] = f2bf(v[r][nt]);
+                }
+            } else {
+                float* C = (float*)L.C;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int m = row_of(mt, r);
+                    if (m >= M) continue;
+                    const long ro = (long)(row0 + m) * L.ldc + ncol;
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) C[ro + nt * 32] = v[r][nt];
+                }
+            }
+        }
     } else if constexpr (EPI == EPI_STORE) {
         bf16_t* C = (bf16_t*)L.C;
-#pragma unroll 1
+#pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {

@@ -97,18 +97,20 @@ def silu(x):
 def conv2d(x, w, b):
     """Same-size convolution with zero padding: x [B, Ci, H, W], w [Co, Ci, k, k]
     (k odd) or [Co, Ci] (1x1), b [Co] -> [B, Co, H, W]."""
+    B, Ci, H, W = x.shape
     if w.ndim == 2:
-        return np.einsum("oi,bihw->bohw", w, x) + b[None, :, None, None]
+        return (w @ x.reshape(B, Ci, H * W)).reshape(B, -1, H, W) + b[None, :, None, None]
     k = w.shape[-1]
     p = k // 2
     xp = np.pad(x, ((0, 0), (0, 0), (p, p), (p, p)))
-    H, W = x.shape[2], x.shape[3]
-    out = np.zeros((x.shape[0], w.shape[0], H, W), dtype=x.dtype)
+    out = np.zeros((B, w.shape[0], H * W), dtype=x.dtype)
     for dy in range(k):
         for dx in range(k):
-            # tap (dy, dx) reads input pixel (y + dy - p, x + dx - p)
-            out += np.einsum("oi,bihw->bohw", w[:, :, dy, dx], xp[:, :, dy:dy + H, dx:dx + W])
-    return out + b[None, :, None, None]
+            # tap (dy, dx) reads input pixel (y + dy - p, x + dx - p); a matrix
+            # product per tap: [Co, Ci] @ [B, Ci, H W]
+            shifted = np.ascontiguousarray(xp[:, :, dy:dy + H, dx:dx + W]).reshape(B, Ci, H * W)
+            out += np.ascontiguousarray(w[:, :, dy, dx]) @ shifted
+    return out.reshape(B, -1, H, W) + b[None, :, None, None]
 
 
 def group_norm(x, groups, gamma, beta, eps):

@@ -30,6 +30,7 @@ SEED_LENGTHS = 3
 SEED_TIMESTEPS = 4
 SEED_ENCODER_WEIGHTS = 5
 SEED_TOKENS = 6
+SEED_VAE_WEIGHTS = 7
 
 
 def _gen(seed: int, index: int) -> np.random.Generator:

@@ -273,3 +273,55 @@ def test_cfg_inputs_library_argument_errors_without_device(af):
     assert lib.af_flow_cfg_inputs(C.c_void_p(4096), 1, 4, 8, 8, 0.5, 0, C.c_void_p(4096 + 512), C.c_void_p(1 << 21),
                                   None) == af.AF_E_INVALID_ARG
     assert "overlaps" in af._lib.af_last_error().decode()
+
+
+# ----------------------------------------------------------------------------- VAE decoder
+
+def _vae_oracle_cfg(c):
+    from oracle import vae as V
+    return V.VAEConfig(latent_channels=c.latent_channels, out_channels=c.out_channels,
+                       block_out_channels=tuple(c.block_out_channels), layers_per_block=c.layers_per_block,
+                       norm_groups=c.norm_groups, norm_eps=float(c.norm_eps), scaling_factor=float(c.scaling_factor))
+
+
+@pytest.mark.parametrize("kw", [{}, dict(block_out_channels=(128, 128, 256, 256), layers_per_block=1)])
+def test_vae_weight_list_matches_oracle(af, kw):
+    """Same names, element counts, order and init recipe as the oracle's decoder list, so
+    seeded weights drawn per index are the same tensors on both sides."""
+    from oracle import vae as V
+    cfg = af.vae_make_config(**kw)
+    specs = V.vae_weight_specs(_vae_oracle_cfg(cfg))
+    n, total = af.af_vae_weight_count(cfg)
+    assert n == len(specs)
+    off = 0
+    for i, (name, shape, kind) in enumerate(specs):
+        nm, r, c, o = af.af_vae_weight_info(cfg, i)
+        assert nm == name and o == off, (i, nm, name)
+        assert r == shape[0] and r * c == int(np.prod(shape)), (nm, r, c, shape)
+        assert af.vae_weight_recipe(nm) == V.vae_weight_recipe(kind), nm
+        off += int(np.prod(shape))
+    assert total == off
+
+
+def test_vae_default_config_matches_oracle_reading(af):
+    from oracle import vae as V
+    c = af.vae_make_config()
+    o = V.VAE_FULL
+    assert (c.latent_channels, c.out_channels, tuple(c.block_out_channels), c.layers_per_block, c.norm_groups) == \
+        (o.latent_channels, o.out_channels, o.block_out_channels, o.layers_per_block, o.norm_groups)
+    assert c.norm_eps == np.float32(o.norm_eps) and c.scaling_factor == np.float32(o.scaling_factor)
+    assert (c.max_batch, c.max_latent_h, c.max_latent_w) == (4, 128, 128)
+
+
+@pytest.mark.parametrize("kw", [dict(block_out_channels=(128, 256, 512, 500)), dict(norm_groups=16),
+                                dict(latent_channels=33), dict(out_channels=5), dict(norm_eps=0.0),
+                                dict(scaling_factor=0.0), dict(block_out_channels=(512, 512, 512, 512)),
+                                dict(max_batch=-1)])
+def test_vae_config_checks(af, kw):
+    with pytest.raises(ValueError):
+        af.af_vae_weight_count(af.vae_make_config(**kw))
+
+
+def test_vae_decode_rejects_null_model(af):
+    assert af._lib.af_vae_decode(None, None, 1, 8, 8, None, None) == af.AF_E_INVALID_ARG
+    assert af._lib.af_vae_decode_taps(None, None, 1, 8, 8, 0, None, None) == af.AF_E_INVALID_ARG
