@@ -11,6 +11,10 @@ input recipe is caught):
                valid lengths                                      [2, 4, 192, 192]
   c1024_mx     the same workload at 1024^2 in MXFP8 mode (oracle mx=True)
                                                                   [2, 4, 128, 128]
+  c1024_mx_ulp the MXFP8 forward of the same inputs with every latent moved up
+               by one float32 ulp: the oracle's own sensitivity, which bounds how
+               closely any implementation that is not bit-identical can agree
+                                                                  [2, 4, 128, 128]
   e1024_b8     samples 1 (uncond, image 1) and 6 (cond, image 2) of the batch-8
                CFG forward of the 4-image sampling workload at step 10 of 25
                (tau = sigma_10, shift 1.73)                       [2, 4, 128, 128]
@@ -67,6 +71,12 @@ def e_inputs():
     return np.concatenate([x0, x0]), tau, oracle.round_bf16(text), mask
 
 
+def ulp_up(inputs):
+    """The same inputs with every latent moved to the next float32 value above it."""
+    lat, taus, text, mask = inputs
+    return np.nextafter(lat, np.float32(np.inf)).astype(np.float32), taus, text, mask
+
+
 def checksum(*arrays):
     return np.array([float(np.asarray(a, np.float64).sum()) for a in arrays], np.float64)
 
@@ -81,6 +91,7 @@ def main():
     jobs = {
         "d1536": lambda: (cd_inputs(192, 192), False, None),
         "c1024_mx": lambda: (cd_inputs(128, 128), True, None),
+        "c1024_mx_ulp": lambda: (ulp_up(cd_inputs(128, 128)), True, None),
         "e1024_b8": lambda: (e_inputs(), False, E_SAMPLES),
     }
     for name, job in jobs.items():

@@ -1,18 +1,21 @@
 """GPU parity of the MXFP8 model (QKV, out-projection and FFN products on MXFP8 operands) against
 the oracle's mx mode, which quantizes the same operands with the same rule
-(oracle/numerics.py mxfp8_qdq, pinned in test_oracle_mxfp8.py) and accumulates
-in float32. Quantization happens at the same points on both sides, but the GPU
-feeds it values that already differ from the fp32 oracle's by the bf16 path's
-own rounding (bf16 q/k/v and attention output, summation order): an element
-whose value moves by a relative delta crosses an E4M3 rounding boundary with
-probability about delta / 2^-3 and then changes by one E4M3 step (2^-3
-relative). At the full width this turns the bf16 path's ~1e-3 block agreement
-into several 1e-3 per block, growing through the blocks, so the bar here is
-max|d|/max|ref| <= 6e-2 and cosine >= 0.998 (measured: the 1 joint + 1 single
-block pair at 512^2 gives 8.1e-3 and 2.5e-2 per block and 3.9e-2 at the output,
-cosine >= 0.9995; the full model at 1024^2 gives 9.0e-3 / 0.99996 after the first
-block and 4.2e-2 / 0.99887 after the fifth). Each comparison also checks that
-the GPU result is closer to the oracle's mx mode than to its plain mode."""
+(oracle/numerics.py mxfp8_qdq, pinned in test_oracle_mxfp8.py), runs attention on
+bf16 operands as the GPU does, and accumulates in float32.
+
+Why the bar is wider than the bf16 path's: E4M3 keeps 3 mantissa bits, so a value
+whose computation differs by a relative delta between two implementations (bf16
+summation order, the exponential's last bit) lands on the other side of an E4M3
+rounding boundary with probability about delta / 2^-3 and then moves by a whole
+E4M3 step. Such flips are rare but each is large, and they compound through the
+blocks. Per block (the block's own update on the GPU's input residual, and the
+chain through the first blocks) the bar is max|d|/max|ref| <= 6e-2 and cosine
+>= 0.998. For the 36-block output the floor is the oracle's own: moving every
+latent by one float32 ulp changes the oracle's mx output by a relative max
+difference of 0.175 and cosine 0.9830 (tests/golden/fullsize_oracle.npz,
+entries c1024_mx and c1024_mx_ulp), so no implementation that is not bit-identical
+can be held closer than that; the output bar is 1.5 times that floor, on both the
+max difference and 1 - cosine."""
 import numpy as np
 import pytest
 
@@ -106,10 +109,17 @@ def test_block_pair_mxfp8_matches_oracle(af):
 
 
 @pytest.mark.timeout(1200)
-def test_full_1024_mxfp8_first_joint_and_single_blocks(af):
+def test_full_1024_mxfp8_whole_forward(af):
     """The full model at 1024^2, CFG batch 2, in MXFP8 mode: the residual after the
     first joint block and after the first single block against the oracle's mx
-    mode, a finite output, and two forwards bit for bit equal."""
+    chain; the own updates of blocks 0, 4, 12, 24 and 35 (the oracle's mx block
+    applied to the GPU's input residual); the 36-block output against the oracle's
+    mx forward, within 1.5 times the oracle's own one-ulp sensitivity (both stored in
+    tests/golden/fullsize_oracle.npz, written from the oracle alone); two forwards
+    bit for bit equal."""
+    import importlib.util
+    import os
+    from helpers import oracle_block_on, update_metrics
     torch = _torch()
     cfg = af.make_config(compute_dtype=af.AF_MXFP8, max_batch=2, max_latent_h=128, max_latent_w=128,
                          max_text_len=256)
@@ -120,34 +130,50 @@ def test_full_1024_mxfp8_first_joint_and_single_blocks(af):
     lat, taus, text, mask = workload_inputs(2, 4, 128, 128, 256, 2048, lengths=lengths, cfg_pairs=True)
     text = oracle.round_bf16(text)
     dev = (to_dev(lat), to_dev(taus), to_dev(text), to_dev(mask))
-    got = {b: m.forward_taps(*dev, stop_after_block=b).cpu().numpy() for b in (0, 4)}
+    upd = (0, 4, 12, 24, 35)
+    got = {b: m.forward_taps(*dev, stop_after_block=b).cpu().numpy()
+           for b in sorted(set(upd) | {b - 1 for b in upd})}
     a = m.forward(*dev).cpu().numpy()
     b = m.forward(*dev).cpu().numpy()
     torch.cuda.synchronize()
     assert np.isfinite(a).all()
     np.testing.assert_array_equal(a, b)
     m.close()
+    here = os.path.dirname(os.path.abspath(__file__))
+    spec = importlib.util.spec_from_file_location("mkg", os.path.join(here, "golden", "make_fullsize_golden.py"))
+    mkg = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mkg)
+    g = np.load(os.path.join(here, "golden", "fullsize_oracle.npz"))
+    np.testing.assert_array_equal(g["c1024_mx_checksum"], mkg.checksum(lat, taus, text, mask))
+    np.testing.assert_array_equal(g["c1024_mx_ulp_checksum"], mkg.checksum(*mkg.ulp_up((lat, taus, text, mask))))
     W = PrefetchWeights(ocfg).as_weights()
     temb, xt, xi, kv = oracle.embed(ocfg, W, lat, taus, text, mask, np.float32)
-    blk = lambda p: {k: W[p + k] for k in ("ada", "wq", "wk", "wv", "wo", "ff1", "ff2", "ff3")}
-    for j in range(ocfg.num_mmdit_layers):
-        xt, xi = oracle.joint_block(ocfg, blk(f"joint{j}.img."), blk(f"joint{j}.txt."), temb, xt, xi, kv,
-                                    np.float32, mx=True)
-        if j == 0:
-            ref0 = np.concatenate([xt, xi], 1)
-    x = oracle.single_block(ocfg, blk("single0."), temb, np.concatenate([xt, xi], 1), kv, np.float32, mx=True)
-    # the same five blocks without quantization
-    temb, pt, pi, kv = oracle.embed(ocfg, W, lat, taus, text, mask, np.float32)
-    for j in range(ocfg.num_mmdit_layers):
-        pt, pi = oracle.joint_block(ocfg, blk(f"joint{j}.img."), blk(f"joint{j}.txt."), temb, pt, pi, kv, np.float32)
-    plain4 = oracle.single_block(ocfg, blk("single0."), temb, np.concatenate([pt, pi], 1), kv, np.float32)
-    for name, g_, r in (("block 0", got[0], ref0), ("block 4", got[4], x)):
-        e, c = rel_max(g_, r), cosine(g_, r)
-        print(f"{name}: rel {e:.3e} cos {c:.6f}")
-        assert e <= TOL and c >= COS, (name, e, c)
-    e_plain = rel_max(got[4], plain4)
-    print(f"block 4 against the oracle without MXFP8: rel {e_plain:.3e} cos {cosine(got[4], plain4):.6f}")
-    assert e_plain > rel_max(got[4], x)
+    Nt = xt.shape[1]
+    # own updates first (each needs only the GPU's input residual and one oracle block)
+    results = []
+    for blk in upd:
+        ref_next = oracle_block_on(ocfg, W, temb, kv, got[blk - 1], blk, Nt, mx=True)
+        e, c = update_metrics(got[blk - 1], got[blk], ref_next)
+        print(f"block {blk} update: rel {e:.3e} cos {c:.6f}", flush=True)
+        results.append((f"block {blk} update", e, c))
+    # chain through block 4
+    x = np.concatenate([xt, xi], 1)
+    chain = {}
+    for blk in range(5):
+        x = oracle_block_on(ocfg, W, temb, kv, x, blk, Nt, mx=True)
+        chain[blk] = x
+    for blk in (0, 4):
+        e, c = rel_max(got[blk], chain[blk]), cosine(got[blk], chain[blk])
+        print(f"block {blk}: rel {e:.3e} cos {c:.6f}", flush=True)
+        results.append((f"block {blk}", e, c))
+    ref = g["c1024_mx"]
+    e_floor, c_floor = rel_max(g["c1024_mx_ulp"], ref), cosine(g["c1024_mx_ulp"], ref)
+    e, c = rel_max(a, ref), cosine(a, ref)
+    print(f"output: rel {e:.3e} cos {c:.6f} (the oracle's own one-ulp sensitivity: rel {e_floor:.3e} "
+          f"cos {c_floor:.6f})", flush=True)
+    for name, e1, c1 in results:
+        assert e1 <= TOL and c1 >= COS, (name, e1, c1)
+    assert e <= 1.5 * e_floor and (1 - c) <= 1.5 * (1 - c_floor), ("output", e, c, e_floor, c_floor)
 
 
 def test_block_pair_mxfp8_non_square_latent(af):
