@@ -1,6 +1,6 @@
-"""The stored oracle outputs in tests/golden/fullsize_oracle.npz: present, finite, of the
-shapes their workloads give, and tied to the current input recipe by the checksums that
-tests/golden/make_fullsize_golden.py records (a change to the seeded input generators
+"""The stored oracle outputs in tests/golden/fullsize_oracle.npz and vae_oracle.npz:
+present, finite, of the shapes their workloads give, and tied to the current input
+recipe by the checksums that the scripts beside them record (a change to the seeded input generators
 or to a workload's recipe fails here, on the CPU, before a GPU run compares against stale
 values)."""
 import importlib.util
@@ -41,3 +41,14 @@ def test_ulp_twin_differs_from_its_base_by_one_ulp_in_the_latents_only():
     assert (lat2 > lat).all()
     np.testing.assert_array_equal(lat2, np.nextafter(lat, np.float32(np.inf)))
     assert taus2 is taus and text2 is text and mask2 is mask
+
+
+def test_stored_vae_decode_matches_its_latent():
+    spec = importlib.util.spec_from_file_location("mkv", os.path.join(HERE, "golden", "make_vae_golden.py"))
+    mkv = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mkv)
+    g = np.load(os.path.join(HERE, "golden", "vae_oracle.npz"))
+    assert float(mkv.latent().astype(np.float64).sum()) == float(g["full1024_checksum"])
+    assert g["full1024_center"].shape == (3, 256, 256) and g["full1024_corners"].shape == (4, 3, 64, 64)
+    for k in ("full1024_center", "full1024_corners", "full1024_mean"):
+        assert np.isfinite(g[k]).all(), k

@@ -99,6 +99,12 @@ def test_small_decoder_every_stage(af):
     _run_case(af, SMALL, 2, 8, 8, 40)
 
 
+def test_small_decoder_odd_latent_and_batch(af):
+    """Narrow decoder, B = 3, a 7 x 9 latent (63 attention keys padded to 128; image 56 x 72,
+    so no level's pixel count is a multiple of a GEMM tile or of a GroupNorm chunk)."""
+    _run_case(af, SMALL, 3, 7, 9, 70)
+
+
 def test_full_width_decoder_non_square(af):
     """The default decoder widths (512/512/256/128, three ResNet blocks per level) on
     a 12 x 20 latent (96 x 160 image; 240 attention keys padded to 256), B = 1."""
@@ -134,6 +140,36 @@ def test_full_size_mid_block_and_batch_independence(af):
     x = V.resnet_block(x, W, "mid.res1", ocfg, np.float32)
     name, e, c = _report("1024^2 mid block, sample 0", mid[:1], x)
     assert e <= TOL and c >= COS, (name, e, c)
+
+
+def test_full_size_image_against_stored_oracle_decode(af):
+    """One 1024 x 1024 image (the first latent of the 4-image sampling workload) decoded
+    whole on the GPU and compared with the oracle's decode of the same latent, stored in
+    tests/golden/vae_oracle.npz (written by tests/golden/make_vae_golden.py from the oracle
+    alone): the central 256 x 256 crop, the four 64 x 64 corners (zero-padding edges at
+    every level) and the per-channel means of the whole image."""
+    import importlib.util
+    import os
+    torch = _torch()
+    here = os.path.dirname(os.path.abspath(__file__))
+    spec = importlib.util.spec_from_file_location("mkv", os.path.join(here, "golden", "make_vae_golden.py"))
+    mkv = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mkv)
+    g = np.load(os.path.join(here, "golden", "vae_oracle.npz"))
+    lat = mkv.latent()
+    assert float(lat.astype(np.float64).sum()) == float(g["full1024_checksum"])
+    m = _decoder(af, {}, 1, 128, 128)
+    img = m.decode(to_dev(lat)).cpu().numpy()
+    torch.cuda.synchronize()
+    m.close()
+    c, k, mean = mkv.crops(img)
+    results = [_report("1024^2 image, centre 256 x 256", c, g["full1024_center"]),
+               _report("1024^2 image, corners", k, g["full1024_corners"])]
+    dm = np.abs(mean - g["full1024_mean"]).max() / np.abs(img).max()
+    print(f"per-channel means: max difference {dm:.3e} of max|image|", flush=True)
+    for name, e, c_ in results:
+        assert e <= TOL and c_ >= COS, (name, e, c_)
+    assert dm <= TOL
 
 
 def test_decode_argument_errors(af):
