@@ -161,6 +161,14 @@ af_status af_init_weights(af_model* m, const float* host_blob, size_t n_floats, 
  *   out         device fp32 [B, out_channels, H, W]
  * The workspace is reused; nothing is allocated. Every kernel of the call is
  * launched on `stream`, in order.
+ * Reproducibility: two calls with the same inputs give bit-identical outputs.
+ * A sample's output does not depend on the other samples' values, but it may
+ * depend on the batch size B (and the latent size): the attention splits the
+ * key range of its last, partial round of query tiles across workgroups, and
+ * which tiles are split depends on the number of tiles, so the fp32 summation
+ * order of a sample's attention - and with it the last bits of its output -
+ * can change with B (differences at the level of fp32 rounding, far inside
+ * the parity bars).
  */
 af_status af_transformer_forward(af_model* m, const float* latents, const float* timestep,
                                  const void* text_embeds, af_dtype text_dtype,

@@ -172,6 +172,25 @@ def test_full_size_image_against_stored_oracle_decode(af):
     assert dm <= TOL
 
 
+def test_decode_before_the_weights_are_complete(af):
+    """A decode before every weight float is loaded returns AF_E_STATE (raised as AfError),
+    and succeeds once the rest is loaded."""
+    import seeded_inputs as si
+    torch = _torch()
+    m = af.VAEDecoder(af.vae_make_config(max_batch=1, max_latent_h=8, max_latent_w=8, **SMALL))
+    lat = torch.zeros((1, 4, 8, 8), dtype=torch.float32, device="cuda")
+    name, rows, cols, off = m.weights[0]
+    m.load_weights(si.normal(si.SEED_VAE_WEIGHTS, 0, (rows * cols,), 0.02), off)
+    with pytest.raises(af.AfError) as e:
+        m.decode(lat)
+    assert e.value.status == af.AF_E_STATE
+    m.load_seeded_weights(threads=16)
+    out = m.decode(lat)
+    torch.cuda.synchronize()
+    assert np.isfinite(out.cpu().numpy()).all()
+    m.close()
+
+
 def test_decode_argument_errors(af):
     torch = _torch()
     m = _decoder(af, SMALL, 2, 8, 8)
