@@ -66,7 +66,6 @@ af_status check_config(const af_vae_config* c) {
     if (c->norm_groups != 32) V_FAIL(AF_E_UNSUPPORTED, "32 GroupNorm groups are built");
     if (c->latent_channels > CIN_PAD) V_FAIL(AF_E_UNSUPPORTED, "at most 32 latent channels");
     if (c->out_channels > 4) V_FAIL(AF_E_UNSUPPORTED, "at most 4 output channels");
-    if (c->block_out_channels[0] > 448) V_FAIL(AF_E_UNSUPPORTED, "the last level's width must be <= 448");
     return AF_OK;
 }
 

@@ -315,7 +315,7 @@ def test_vae_default_config_matches_oracle_reading(af):
 
 @pytest.mark.parametrize("kw", [dict(block_out_channels=(128, 256, 512, 500)), dict(norm_groups=16),
                                 dict(latent_channels=33), dict(out_channels=5), dict(norm_eps=0.0),
-                                dict(scaling_factor=0.0), dict(block_out_channels=(512, 512, 512, 512)),
+                                dict(scaling_factor=0.0), dict(block_out_channels=(128, 256, 512, 1152)),
                                 dict(max_batch=-1)])
 def test_vae_config_checks(af, kw):
     with pytest.raises(ValueError):
