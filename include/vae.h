@@ -29,7 +29,7 @@
  * are fp32. bf16 has fp32's exponent range, so the overflow that the fp16
  * upcast avoids does not arise.
  *
- * Built configurations: 4 up levels; every block width a multiple of 128;
+ * Built configurations: 4 up levels; every block width a multiple of 128, at most 1024;
  * norm_groups 32; latent_channels <= 32; out_channels <= 4; latent sizes up to
  * max_latent_h x max_latent_w. Others return AF_E_UNSUPPORTED.
  */
