@@ -321,17 +321,29 @@ void k_attention_bf16(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K
 
     // lane has query q0 + (lane & 31), head dims ht*32 + i*8 + 4 (lane>>5) + j
     const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    // The outputs leave through LDS: in the accumulator layout a store instruction
+    // would write 16 (bf16) or 32 (fp32) bytes per query row; staged, every
+    // instruction writes whole rows. Each wave stages and reads back only its own
+    // 32 rows, after one barrier that ends every wave's reads of the K and v^T slots.
     if (piece >= 0) {
-        // a piece: unnormalised partial O and its sum of p, fp32
-        float* blk = part + (size_t)piece * (QT * HD + QT);
-        const int ql = wave * 32 + l32;
+        // a piece: unnormalised partial O and its sum of p, fp32. Staging: the
+        // wave's 32 rows of 1 KB, 16-byte chunk c of row r at c ^ (r & 31).
+        __syncthreads();
+        float* st = reinterpret_cast<float*>(smem) + wave * 32 * HD;
 #pragma unroll
         for (int ht = 0; ht < 8; ++ht)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                *reinterpret_cast<float4*>(blk + ql * HD + ht * 32 + i * 8 + grp * 4) =
+                *reinterpret_cast<float4*>(st + l32 * HD + (((ht * 8 + i * 2 + grp) ^ l32) * 4)) =
                     make_float4(o[ht][i * 4 + 0], o[ht][i * 4 + 1], o[ht][i * 4 + 2], o[ht][i * 4 + 3]);
-        if (grp == 0) blk[QT * HD + ql] = l_tot;
+        __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's staging writes are done
+        __builtin_amdgcn_wave_barrier();
+        float* blk = part + (size_t)piece * (QT * HD + QT) + (size_t)(wave * 32) * HD;
+#pragma unroll 8
+        for (int r = 0; r < 32; ++r)
+            *reinterpret_cast<float4*>(blk + r * HD + lane * 4) =
+                *reinterpret_cast<const float4*>(st + r * HD + ((lane ^ r) * 4));
+        if (grp == 0) part[(size_t)piece * (QT * HD + QT) + QT * HD + wave * 32 + l32] = l_tot;
         return;
     }
     // ---- normalise and store (a query whose keys are all excluded gets zeros)
@@ -362,16 +374,27 @@ void k_attention_bf16(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K
         }
         return;
     }
-    if (q < S) {
-        bf16_t* orow = O + (long)g.row_of(b, q) * d + h * HD + grp * 4;
+    // bf16 output. Staging: the wave's 32 rows of 512 B, 16-byte chunk c of row r
+    // at c ^ (r & 31); a lane's four values are one half of a chunk.
+    __syncthreads();
+    bf16_t* st = smem + wave * 32 * HD;
 #pragma unroll
-        for (int ht = 0; ht < 8; ++ht)
+    for (int ht = 0; ht < 8; ++ht)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                uint2 v = make_uint2(pack2bf(o[ht][i * 4 + 0] * inv, o[ht][i * 4 + 1] * inv),
-                                     pack2bf(o[ht][i * 4 + 2] * inv, o[ht][i * 4 + 3] * inv));
-                *reinterpret_cast<uint2*>(orow + ht * 32 + i * 8) = v;
-            }
+        for (int i = 0; i < 4; ++i)
+            *reinterpret_cast<uint2*>(st + l32 * HD + (((ht * 4 + i) ^ l32) * 8) + grp * 4) =
+                make_uint2(pack2bf(o[ht][i * 4 + 0] * inv, o[ht][i * 4 + 1] * inv),
+                           pack2bf(o[ht][i * 4 + 2] * inv, o[ht][i * 4 + 3] * inv));
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's staging writes are done
+    __builtin_amdgcn_wave_barrier();
+    // one instruction = two rows: lanes 0-31 row 2 k, lanes 32-63 row 2 k + 1,
+    // 16 bytes each (logical chunk lane & 31)
+#pragma unroll 4
+    for (int k = 0; k < 16; ++k) {
+        const int r = 2 * k + grp;
+        const int qr = q0 + r;
+        const uint4 v = *reinterpret_cast<const uint4*>(st + r * HD + ((l32 ^ r) * 8));
+        if (qr < S) *reinterpret_cast<uint4*>(O + (long)g.row_of(b, qr) * d + h * HD + l32 * 8) = v;
     }
 }
 
