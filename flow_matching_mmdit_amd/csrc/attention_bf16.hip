@@ -52,6 +52,8 @@ constexpr int HD = 256;
 constexpr int QT = 128;  // queries per workgroup
 constexpr int KT = 64;   // keys per tile
 constexpr int KTILE = KT * HD;   // bf16 elements of a K (or v^T) tile
+// s_waitcnt immediate: vmcnt(17) (bits 3:0 and 15:14), expcnt and lgkmcnt not waited
+constexpr int VMCNT_17 = (17 & 15) | ((17 >> 4) << 14) | (7 << 4) | (15 << 8);
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -150,39 +152,42 @@ void k_attention_bf16(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K
     };
 
     // The wave's 32 queries as MFMA B operands: lane holds query q0 + (lane & 31),
-    // head dims [16 s + 8 (lane >> 5), +8) for k-step s. The workgroup's 128 x 256
-    // query tile is staged through the (still idle) v^T slots so the registers
-    // come from LDS reads.
+    // head dims [16 s + 8 (lane >> 5), +8) for k-step s, loaded straight into
+    // registers. K of tiles 0 and 1, the bias of tile 1 and v^T of tile 0 go out at
+    // the same time; the wait before the first barrier covers the queries, the
+    // bias of tile 0 and K(0) (the 17 direct loads issued after them may still be
+    // in flight).
     bf16x8 qf[16];
+    // the bias of tile 0 for the first S tile, in the accumulator order of s_init
+    // below, also straight into registers (an LDS read issued behind the direct
+    // loads would wait for all of them)
+    float4 bias0[8];
     {
-        bf16_t* sQ = vslot(0);                         // 64 KB: rows of 512 B
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                bias0[t * 4 + i] = *reinterpret_cast<const float4*>(biasb + kt0 * KT + t * 32 + (i >> 1) * 16 + grp * 8 +
+                                                                    (i & 1) * 4);
         const bf16_t* qsrc = Q + (bh * S_pad + (long)qt * QT) * HD;
         const __amdgpu_buffer_rsrc_t rQ = __builtin_amdgcn_make_buffer_rsrc((void*)qsrc, (short)0, QT * HD * 2, 0x00020000);
-        // 128 rows x 32 chunks = 64 instructions of 1 KB, 16 per wave; lane -> row
-        // 2 cb + (lane >> 5), physical chunk lane & 31, logical chunk pc ^ (row & 31).
+        const int row = wave * 32 + l32;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            int cb = wave * 16 + j;
-            int row = 2 * cb + grp;
-            int lc = (lane & 31) ^ (row & 31);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rQ, (lds_void*)(sQ + cb * 512), 16, (row * HD + lc * 8) * 2, 0, 0, 0);
+        for (int s2 = 0; s2 < 16; ++s2) {
+            typedef int i32x4 __attribute__((ext_vector_type(4)));
+            const i32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rQ, (row * HD + (2 * s2 + grp) * 8) * 2, 0, 0);
+            qf[s2] = __builtin_bit_cast(bf16x8, v);
         }
-        // K and the bias of tiles 0 and 1 go out meanwhile (their slots are not the Q stage)
 #pragma unroll
         for (int j = 0; j < 8; ++j) issue_k(j, 0, 0);
-        issue_b(0, 0);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) issue_v(j, 0, 0);
 #pragma unroll
         for (int j = 0; j < 8; ++j) issue_k(j, 1, 1);
         issue_b(1, 1);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        const int row = wave * 32 + l32;
-#pragma unroll
-        for (int s = 0; s < 16; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(sQ + row * HD + (((2 * s + grp) ^ (row & 31)) * 8));
-        __syncthreads();
+        __builtin_amdgcn_s_waitcnt(VMCNT_17);
+        __builtin_amdgcn_s_barrier();
     }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) issue_v(j, 0, 0);
 
     f32x16 o[8];
 #pragma unroll
@@ -228,7 +233,15 @@ void k_attention_bf16(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K
     // Prologue: S of tile 0 (K slot 0).
     f32x16 sa[2], sb[2];
     {
-        s_init(sa, 0);
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                sa[t][i * 4 + 0] = bias0[t * 4 + i].x;
+                sa[t][i * 4 + 1] = bias0[t * 4 + i].y;
+                sa[t][i * 4 + 2] = bias0[t * 4 + i].z;
+                sa[t][i * 4 + 3] = bias0[t * 4 + i].w;
+            }
         const bf16_t* sK = kslot(0);
         bf16x8 kf[KD + 1][2];
 #pragma unroll
