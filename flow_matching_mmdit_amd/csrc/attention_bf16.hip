@@ -278,6 +278,15 @@ void k_attention_bf16(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K
         bf16x8 pb[4];
         float pf[8];
         float psum = 0.f;
+        // v^T(t) is in slot c since this iteration's barrier
+        const bf16_t* sV = vslot(c);
+        bf16x8 vf[VD + 1];
+        auto vload = [&](int idx, bf16x8& dst) {      // idx = s4 * 8 + ht
+            const int s4 = idx >> 3, ht = idx & 7;
+            const int row = ht * 32 + l32;
+            const int ch = (2 * s4 + grp) ^ vswz(row);
+            dst = *reinterpret_cast<const bf16x8*>(sV + row * KT + ch * 8);
+        };
         // p value k (0..31) of S(t): key step s4 = k / 8, element e = k % 8
         auto p_step = [&](int k) {
             const int e = k & 7, s4 = k >> 3;
@@ -289,6 +298,7 @@ void k_attention_bf16(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K
 #pragma unroll
         for (int s = 0; s < 16; ++s) {
             if (s + KD < 16) kload(sK, s + KD, kf[(s + KD) % (KD + 1)]);
+            if (s >= 16 - VD) vload(s - (16 - VD), vf[s - (16 - VD)]);
             // this iteration's direct loads all go out during the S MFMAs, a
             // whole P V phase ahead of the wait at the next iteration's barrier
             if ((s & 1) == 0) issue_k(s >> 1, t + 2, c);
@@ -303,17 +313,8 @@ void k_attention_bf16(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K
         }
 
         // ---- O^T += V^T P^T for tile t: 8 independent head-dim chains per key
-        //      step, v^T fragments read VD MFMAs ahead
-        const bf16_t* sV = vslot(c);
-        bf16x8 vf[VD + 1];
-        auto vload = [&](int idx, bf16x8& dst) {      // idx = s4 * 8 + ht
-            const int s4 = idx >> 3, ht = idx & 7;
-            const int row = ht * 32 + l32;
-            const int ch = (2 * s4 + grp) ^ vswz(row);
-            dst = *reinterpret_cast<const bf16x8*>(sV + row * KT + ch * 8);
-        };
-#pragma unroll
-        for (int x = 0; x < VD; ++x) vload(x, vf[x]);
+        //      step, v^T fragments read VD MFMAs ahead (the first VD during the
+        //      last S steps)
 #pragma unroll
         for (int x = 0; x < 32; ++x) {
             if (x + VD < 32) vload(x + VD, vf[(x + VD) % (VD + 1)]);
