@@ -41,8 +41,11 @@
 // keeps the compiler's LDS-read waits partial) issued one per S MFMA step: in
 // iteration t, K and the bias of tile t + 2 and v^T of tile t + 1, so each has
 // the whole P V phase to land before the next iteration's wait. One barrier per
-// iteration publishes them and frees the slots. 16-byte chunks are
-// XOR swizzled by row so both operand reads are bank-conflict free.
+// iteration publishes them and frees the slots; the first v^T fragments of a
+// P V phase are read during the last S steps. 16-byte chunks are XOR swizzled by
+// row so both operand reads are bank-conflict free. The query fragments are
+// loaded straight into registers; the output leaves through LDS, whole rows per
+// store instruction.
 #include "af_internal.h"
 
 namespace af {
