@@ -430,7 +430,8 @@ def loop_leg(af, torch, model, cfg, loops, warmup_loops, imgs=4, H=128, W=128, T
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 20 forwards; 10 loops with --sampling-loop)")
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default="1024")
     ap.add_argument("--latent", default=None, metavar="HxW",
@@ -459,6 +460,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run the plain 512 MiB device copy used to scale the HBM byte counters")
     args = ap.parse_args()
+    if args.steps is None:
+        args.steps = 10 if args.sampling_loop else 20
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the forward runs on a single MI355X and this build has no "
               f"multi-GPU path (--gpus {args.gpus} requested).", file=sys.stderr)
