@@ -38,7 +38,7 @@ import numpy as np  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA, published
-MX_CLASSES = ("gemm_qkv", "gemm_ffn_up", "gemm_ffn_down")   # products on MXFP8 operands in --mxfp8 runs
+MX_CLASSES = ("gemm_qkv", "gemm_out", "gemm_ffn_up", "gemm_ffn_down")   # products on MXFP8 operands in --mxfp8 runs
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
 
 WORKLOADS = {
